@@ -1,0 +1,274 @@
+"""Seeded synthetic inputs for the MoE expert layer with per-request LoRA deltas.
+
+This module only *generates inputs*: request segments, adapter slots, router
+outputs, expert weights and LoRA pools.  It holds none of the layer's own
+arithmetic (no projection, activation, LoRA delta or combine), so that both the
+HIP path and the CPU oracle can be fed from it without sharing any computation.
+It imports nothing else from this package.
+
+Shapes and distributions follow the workloads of the MoE-LoRA pages
+(SGLang PR #14105 "LoRA on MoE expert layers", section "实现拆解": the 4-D pool
+[num_loras, num_experts, rank, dim]; SGLang PR #24160, section "关键源码片段":
+int32 segment / adapter metadata).  Conventions fixed here where the pages are
+silent:
+
+* ``N(m, v)`` takes ``v`` as the variance: W ~ N(0, 1/fan_in), A ~ N(0, 1/in),
+  B ~ N(0, 0.01) (std 0.1).
+* Pools are rank-major: A as [L, E, R, in], B stored transposed as
+  [L, E, R, out].  Rows at index >= the slot rank are NaN when ``canary`` is
+  set (they must never be read) and 0 otherwise.
+* Router: float64 softmax over experts, top-k by descending probability with
+  ties going to the lower expert id, weights renormalised over the top-k and
+  stored as float32.
+* Each tensor (and each expert slice of it) has its own sub-seed derived from
+  ``(seed, tensor_id, expert)``, so any expert can be regenerated on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+# tensor ids for sub-seeds
+_TID_X, _TID_WGU, _TID_WD = 1, 2, 3
+_TID_AG, _TID_AU, _TID_BG, _TID_BU, _TID_AD, _TID_BD = 4, 5, 6, 7, 8, 9
+_TID_ROUTER, _TID_LENS, _TID_WI, _TID_RANKS, _TID_BIAS = 10, 11, 12, 13, 14
+
+
+@dataclasses.dataclass
+class LayerSpec:
+    """One MoE-LoRA layer plus one batch of requests."""
+    name: str
+    num_experts: int
+    top_k: int
+    hidden: int
+    inter: int
+    num_loras: int
+    lora_ranks: List[int]
+    seg_lens: List[int]
+    weight_indices: List[int]
+    dtype: str = "bf16"          # "bf16" or "f32": x, weights, pools and y
+    seed: int = 0
+    router: str = "normal"       # "normal" | "zipf" | "uniform_bias"
+    alpha_over_rank: float = 2.0  # scaling = alpha / r with alpha = 2r
+    pool_rank: Optional[int] = None
+
+    @property
+    def num_tokens(self) -> int:
+        return int(sum(self.seg_lens))
+
+    @property
+    def num_reqs(self) -> int:
+        return len(self.seg_lens)
+
+    @property
+    def max_rank(self) -> int:
+        if self.pool_rank is not None:
+            return int(self.pool_rank)
+        return max([int(r) for r in self.lora_ranks] + [1])
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+def _subseed(*key: int) -> int:
+    ss = np.random.SeedSequence([int(k) & 0xFFFFFFFF for k in key])
+    return int(ss.generate_state(1, np.uint64)[0] & ((1 << 63) - 1))
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(_subseed(*key))
+
+
+def _lengths_with_total(rng: np.random.Generator, bs: int, total: int,
+                        lo: int = 64, hi: int = 512) -> List[int]:
+    """Request lengths drawn U{lo..hi}, then nudged one token at a time (a seeded
+    random request, staying within [lo, hi]) until they sum to ``total``."""
+    if not (bs * lo <= total <= bs * hi):
+        raise ValueError("total not reachable with lengths in [lo, hi]")
+    lens = rng.integers(lo, hi + 1, size=bs).astype(np.int64)
+    while lens.sum() != total:
+        b = int(rng.integers(0, bs))
+        if lens.sum() > total and lens[b] > lo:
+            lens[b] -= 1
+        elif lens.sum() < total and lens[b] < hi:
+            lens[b] += 1
+    return [int(v) for v in lens]
+
+
+def config(name: str) -> LayerSpec:
+    """The six named workloads (c4 has a prefill batch and a decode batch)."""
+    if name == "c0":
+        # tiny fp32 layer, request structure of the pages' worked example
+        return LayerSpec("c0_tiny_fp32", 8, 2, 256, 512, 4, [0, 8, 8, 16],
+                         [5, 1, 7, 3, 9, 2], [2, 0, 3, 2, -1, 1],
+                         dtype="f32", seed=0, router="normal", pool_rank=16)
+    if name == "c1":
+        seed = 1
+        rng = _rng(seed, _TID_LENS)
+        lens = _lengths_with_total(rng, 16, 4096)
+        rng = _rng(seed, _TID_WI)
+        wi = rng.integers(0, 8, size=16)
+        neg = rng.choice(16, size=2, replace=False)   # 10% of 16 requests -> 2
+        wi[neg] = -1
+        ranks = [0] + [16] * 7
+        return LayerSpec("c1_mixtral_prefill", 8, 2, 4096, 14336, 8, ranks, lens,
+                         [int(v) for v in wi], seed=seed, router="normal",
+                         pool_rank=16)
+    if name == "c2":
+        seed = 2
+        lens = _lengths_with_total(_rng(seed, _TID_LENS), 32, 8192)
+        ranks = _rng(seed, _TID_RANKS).choice([0, 8, 16, 32, 64], size=16)
+        wi = _rng(seed, _TID_WI).integers(0, 16, size=32)
+        return LayerSpec("c2_finegrained_prefill", 128, 8, 2048, 768, 16,
+                         [int(r) for r in ranks], lens, [int(v) for v in wi],
+                         seed=seed, router="zipf",
+                         pool_rank=int(max(ranks)) if max(ranks) > 0 else 8)
+    if name == "c3":
+        return LayerSpec("c3_decode", 128, 8, 2048, 768, 32, [32] * 32, [1] * 64,
+                         [b % 32 for b in range(64)], seed=3, router="normal",
+                         pool_rank=32)
+    if name in ("c4p", "c4d"):
+        if name == "c4p":
+            lens = _lengths_with_total(_rng(4, _TID_LENS), 64, 16384)
+            wi = [int(v) for v in _rng(4, _TID_WI).integers(0, 8, size=64)]
+        else:
+            lens = [1] * 128
+            wi = [b % 8 for b in range(128)]
+        return LayerSpec(f"{name}_large_expert_{'prefill' if name == 'c4p' else 'decode'}",
+                         256, 8, 7168, 2048, 8, [32] * 8, lens, wi, seed=4,
+                         router="uniform_bias", pool_rank=32)
+    raise KeyError(name)
+
+
+CONFIG_NAMES = ("c0", "c1", "c2", "c3", "c4p", "c4d")
+
+
+# ----------------------------------------------------------------------------
+# router (input generation only; the layer takes topk_ids / topk_weights)
+# ----------------------------------------------------------------------------
+def router_logits(spec: LayerSpec) -> np.ndarray:
+    T, E = spec.num_tokens, spec.num_experts
+    # c4p and c4d share the layer, hence the bias; the token logits differ per batch
+    tok_key = 0 if spec.name.startswith("c4d") else 1
+    rng = _rng(spec.seed, _TID_ROUTER, tok_key)
+    if spec.router == "normal":
+        return rng.standard_normal((T, E))
+    if spec.router == "zipf":
+        # popularity in softmax space ~ rank^-1.1 over a seeded permutation
+        perm = _rng(spec.seed, _TID_BIAS).permutation(E) + 1
+        bias = -1.1 * np.log(perm.astype(np.float64))
+        return rng.standard_normal((T, E)) + bias[None, :]
+    if spec.router == "uniform_bias":
+        bias = _rng(spec.seed, _TID_BIAS).normal(0.0, np.sqrt(2.0), size=E)
+        return rng.uniform(0.0, 1.0, size=(T, E)) + bias[None, :]
+    raise ValueError(spec.router)
+
+
+def route(logits: np.ndarray, k: int):
+    """softmax -> top-k (ties to the lower expert id) -> renormalise."""
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")[:, :k]
+    ids = order.astype(np.int32)
+    w = np.take_along_axis(p, order, axis=1)
+    w = w / w.sum(axis=1, keepdims=True)
+    return ids, w.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# tensors
+# ----------------------------------------------------------------------------
+def _randn(shape, std: float, seed: int, device, dtype) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def generate(spec: LayerSpec, device="cpu", canary: bool = True,
+             with_lora: bool = True) -> Dict[str, object]:
+    """Every input of the layer for ``spec`` as tensors on ``device``.
+
+    Integer metadata is int32, router weights and scaling float32, the rest in
+    ``spec.dtype``.  Returns a dict; ``meta`` holds the host copies of the
+    request metadata.
+    """
+    dev = torch.device(device)
+    dt = spec.torch_dtype
+    T, E, k, H, I = spec.num_tokens, spec.num_experts, spec.top_k, spec.hidden, spec.inter
+    L, R = spec.num_loras, spec.max_rank
+    s = spec.seed
+
+    seg_lens = np.asarray(spec.seg_lens, dtype=np.int64)
+    seg_indptr = np.zeros(len(seg_lens) + 1, dtype=np.int32)
+    seg_indptr[1:] = np.cumsum(seg_lens)
+    wi = np.asarray(spec.weight_indices, dtype=np.int32)
+    ranks = np.asarray(spec.lora_ranks, dtype=np.int32)
+    scaling = np.full(L, spec.alpha_over_rank, dtype=np.float32)
+    ids, w = route(router_logits(spec), k)
+
+    out: Dict[str, object] = {}
+    x_key = 0 if not spec.name.startswith("c4d") else 1
+    out["x"] = _randn((T, H), 1.0, _subseed(s, _TID_X, x_key), dev, dt)
+    wgu = torch.empty((E, 2 * I, H), device=dev, dtype=dt)
+    wd = torch.empty((E, H, I), device=dev, dtype=dt)
+    for e in range(E):
+        wgu[e] = _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, dt)
+        wd[e] = _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, dt)
+    out["w_gate_up"], out["w_down"] = wgu, wd
+
+    if with_lora and L > 0:
+        fill = float("nan") if canary else 0.0
+        pools = {}
+        for name, tid, dim, std in (("a_gate", _TID_AG, H, 1.0 / np.sqrt(H)),
+                                    ("a_up", _TID_AU, H, 1.0 / np.sqrt(H)),
+                                    ("b_gate", _TID_BG, I, 0.1),
+                                    ("b_up", _TID_BU, I, 0.1),
+                                    ("a_down", _TID_AD, I, 1.0 / np.sqrt(I)),
+                                    ("b_down", _TID_BD, H, 0.1)):
+            pool = torch.full((L, E, R, dim), fill, device=dev, dtype=dt)
+            for l in range(L):
+                r = int(ranks[l])
+                if r == 0:
+                    continue
+                for e in range(E):
+                    pool[l, e, :r] = _randn((r, dim), std, _subseed(s, tid, l * 65536 + e), dev, dt)
+            pools[name] = pool
+        out.update(pools)
+    out["topk_ids"] = torch.from_numpy(ids).to(dev)
+    out["topk_weights"] = torch.from_numpy(w).to(dev)
+    out["seg_indptr"] = torch.from_numpy(seg_indptr).to(dev)
+    out["weight_indices"] = torch.from_numpy(wi).to(dev)
+    out["lora_ranks"] = torch.from_numpy(ranks).to(dev)
+    out["scaling"] = torch.from_numpy(scaling).to(dev)
+    out["meta"] = dict(seg_indptr=seg_indptr, weight_indices=wi, lora_ranks=ranks,
+                       scaling=scaling, topk_ids=ids, topk_weights=w,
+                       max_seg_len=int(seg_lens.max()) if len(seg_lens) else 0)
+    return out
+
+
+def random_spec(rng: np.random.Generator, *, max_experts=6, max_k=3, max_dim=96,
+                max_loras=4, max_rank=8, max_reqs=5, max_len=6, dtype="f32",
+                name="random") -> LayerSpec:
+    """A small random layer (dims multiples of 8) for fuzz and property tests."""
+    E = int(rng.integers(1, max_experts + 1))
+    k = int(rng.integers(1, min(max_k, E) + 1))
+    H = 8 * int(rng.integers(1, max_dim // 8 + 1))
+    I = 8 * int(rng.integers(1, max_dim // 8 + 1))
+    L = int(rng.integers(0, max_loras + 1))
+    R = int(rng.integers(1, max_rank + 1))
+    ranks = [int(v) for v in rng.integers(0, R + 1, size=L)]
+    bs = int(rng.integers(1, max_reqs + 1))
+    lens = [int(v) for v in rng.integers(0, max_len + 1, size=bs)]
+    if sum(lens) == 0:
+        lens[0] = 1
+    wi = [int(v) for v in rng.integers(-1, L, size=bs)] if L > 0 else [-1] * bs
+    return LayerSpec(name, E, k, H, I, L, ranks, lens, wi, dtype=dtype,
+                     seed=int(rng.integers(0, 2**31)), router="normal", pool_rank=R)

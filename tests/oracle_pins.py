@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` takes an oracle module (the real one, or a mutant planted by
+``test_oracle_mutants.py``) and raises AssertionError when the oracle disagrees
+with what the pages or the mathematics fix:
+
+* worked vectors of the PR #24160 page (section 关键源码片段) and their
+  closed forms, evaluated with library routines (numpy repeat / scatter);
+* numpy's stable lexsort and a Python ``sorted`` brute force for the align
+  layout, plus its invariants;
+* torch's own linear / SiLU layers (a PEFT-style LoRA module built from
+  ``torch.nn.functional.linear``) for the layer formula of the PR #14105 page,
+  section 实现拆解;
+* algebraic identities: LoRA == merged weights, linearity of the down delta in
+  B_d, invariance under permuting top-k slots and requests, identical experts,
+  exact reduction to the base MoE when B = 0, rank = 0 or slot = -1.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from moe_expert_layer_segment_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def np_inputs(spec, canary=True, with_lora=True):
+    """Inputs of ``spec`` generated on the CPU, as float64 / int numpy arrays."""
+    d = workloads.generate(spec, device="cpu", canary=canary, with_lora=with_lora)
+    out = {}
+    for key, v in d.items():
+        if key == "meta":
+            continue
+        if v.dtype in (torch.int32, torch.int64):
+            out[key] = v.numpy().copy()
+        else:
+            out[key] = v.float().numpy().astype(np.float64)
+    out["meta"] = d["meta"]
+    out["spec"] = spec
+    return out
+
+
+def info_of(orc, inp):
+    m = inp["meta"]
+    return orc.moe_lora_info(int(m["seg_indptr"][-1]), m["seg_indptr"], m["weight_indices"],
+                             m["lora_ranks"], m["max_seg_len"])
+
+
+def fwd(orc, inp, fn="moe_lora_forward", lora=True, **over):
+    enabled, mapping = info_of(orc, inp)
+    kw = dict(x=inp["x"], topk_ids=inp["topk_ids"], topk_weights=inp["topk_weights"],
+              w_gate_up=inp["w_gate_up"], w_down=inp["w_down"],
+              lora_ranks=inp["lora_ranks"], scaling=inp["scaling"],
+              token_lora_mapping=mapping, adapter_enabled=enabled)
+    if lora and "a_gate" in inp:
+        for n in ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down"):
+            kw[n] = inp[n]
+    kw.update(over)
+    return getattr(orc, fn)(**kw)
+
+
+def rel_l2(a, b):
+    d = np.linalg.norm(np.asarray(a) - np.asarray(b))
+    n = np.linalg.norm(np.asarray(b))
+    return d / max(n, 1e-300)
+
+
+def tiny_spec(seed=0, **kw):
+    base = dict(num_experts=4, top_k=2, hidden=24, inter=40, num_loras=3,
+                lora_ranks=[4, 0, 6], seg_lens=[3, 0, 4, 2], weight_indices=[2, 1, 0, -1],
+                dtype="f32", seed=seed, router="normal", pool_rank=8)
+    base.update(kw)
+    return workloads.LayerSpec(name="tiny", **base)
+
+
+# ---------------------------------------------------------------------------
+# info
+# ---------------------------------------------------------------------------
+def pin_info_page_vector(orc):
+    g = _load("info_page_vector.json")
+    lens = np.array(g["seg_lens"])
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    en, mp = orc.moe_lora_info(int(indptr[-1]), indptr, g["weight_indices"], g["lora_ranks"],
+                               g["max_len"])
+    assert mp.tolist() == g["expected_token_lora_mapping"]
+    assert en.tolist() == g["expected_adapter_enabled"]
+    # the test's closed forms evaluated with library routines
+    wi = np.array(g["weight_indices"])
+    assert np.array_equal(mp, np.repeat(wi, lens))
+    ranks = np.array(g["lora_ranks"])
+    exp = np.zeros_like(ranks)
+    np.put(exp, wi, (ranks[wi] > 0).astype(ranks.dtype))
+    assert np.array_equal(en, exp)
+
+
+def pin_info_config0(orc):
+    g = _load("info_config0.json")
+    lens = np.array(g["seg_lens"])
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    en, mp = orc.moe_lora_info(int(indptr[-1]), indptr, g["weight_indices"], g["lora_ranks"], 9)
+    assert mp.tolist() == g["expected_token_lora_mapping"]
+    assert en.tolist() == g["expected_adapter_enabled"]
+
+
+def pin_info_undercover(orc):
+    g = _load("info_undercover.json")
+    try:
+        orc.moe_lora_info(g["num_tokens"], g["seg_indptr"], g["weight_indices"],
+                          g["lora_ranks"], g["max_len"])
+    except AssertionError as exc:
+        assert g["message"] in str(exc)
+    else:
+        raise AssertionError("under-covered launch was accepted")
+    # the same batch with a covering max_len is fine
+    en, mp = orc.moe_lora_info(300, g["seg_indptr"], g["weight_indices"], g["lora_ranks"], 300)
+    assert mp.tolist() == [0] * 300 and en.tolist() == [1]
+
+
+def pin_info_random(orc):
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        bs = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 7))
+        lens = rng.integers(0, 6, size=bs)
+        indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        wi = rng.integers(-1, L, size=bs)
+        ranks = rng.choice([0, 4, 8], size=L)
+        en, mp = orc.moe_lora_info(int(indptr[-1]), indptr, wi, ranks, int(lens.max()))
+        # brute force over tokens / slots
+        T = int(indptr[-1])
+        for t in range(T):
+            b = max(i for i in range(bs) if indptr[i] <= t)
+            assert mp[t] == wi[b]
+        for i in range(L):
+            used = any(int(w) == i for w in wi)
+            assert en[i] == int(used and ranks[i] > 0)
+
+
+# ---------------------------------------------------------------------------
+# align
+# ---------------------------------------------------------------------------
+def _rand_align_case(rng, T, k, E, L):
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) \
+        if T > 0 else np.zeros((0, k), np.int32)
+    mapping = rng.integers(-1, L, size=T).astype(np.int32) if L > 0 else np.full(T, -1, np.int32)
+    enabled = rng.integers(0, 2, size=L).astype(np.int32)
+    return ids, mapping, enabled
+
+
+def pin_align_lexsort(orc):
+    rng = np.random.default_rng(11)
+    for (T, k, E, L, BM) in [(37, 2, 8, 4, 16), (200, 4, 16, 3, 16), (5, 1, 3, 0, 32),
+                             (300, 8, 64, 5, 16), (1, 1, 1, 1, 16)]:
+        ids, mapping, enabled = _rand_align_case(rng, T, k, E, L)
+        out = orc.moe_lora_align(ids, mapping, enabled, E, L, BM)
+        P = T * k
+        e = ids.reshape(-1).astype(np.int64)
+        tok = np.repeat(np.arange(T), k)
+        a = np.where((mapping[tok] >= 0) & (enabled[np.maximum(mapping[tok], 0)] == 1),
+                     mapping[tok], -1) if L > 0 else np.full(P, -1)
+        p = np.arange(P)
+        order = np.lexsort((p, a, e))        # library stable sort: e, then a, then p
+        got = out["sorted_pair_ids"]
+        real = got[got < P]
+        assert np.array_equal(real, order)
+        # bucket tables against np.unique counts
+        keys, counts = np.unique(np.stack([e[order], a[order]]), axis=1, return_counts=True)
+        row = 0
+        for (ee, aa), c in zip(keys.T, counts):
+            nt = -(-int(c) // BM)
+            assert np.all(got[row:row + c] == order[np.flatnonzero((e[order] == ee) & (a[order] == aa))])
+            assert np.all(got[row + c:row + nt * BM] == P)
+            assert np.all(out["tile_expert"][row // BM: row // BM + nt] == ee)
+            assert np.all(out["tile_lora"][row // BM: row // BM + nt] == aa)
+            row += nt * BM
+        assert out["num_rows_padded"][0] == row
+        assert np.all(got[row:] == P)
+        assert np.all(out["tile_expert"][row // BM:] == -1)
+        assert np.all(out["tile_lora"][row // BM:] == -1)
+        assert row <= got.shape[0] == orc.align_capacity_rows(P, E, L, BM)
+
+
+def pin_align_bruteforce(orc):
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        T, k = int(rng.integers(0, 7)), int(rng.integers(1, 3))
+        E = int(rng.integers(k, 5))
+        L = int(rng.integers(0, 3))
+        BM = 16
+        ids, mapping, enabled = _rand_align_case(rng, T, k, E, L)
+        out = orc.moe_lora_align(ids, mapping, enabled, E, L, BM)
+        P = T * k
+        pairs = []
+        for p in range(P):
+            t, j = divmod(p, k)
+            m = int(mapping[t]) if L > 0 else -1
+            a = m if (m >= 0 and enabled[m] == 1) else -1
+            pairs.append((int(ids[t, j]), a, p))
+        pairs = sorted(pairs)
+        rows, te, tl = [], [], []
+        i = 0
+        while i < len(pairs):
+            j = i
+            while j < len(pairs) and pairs[j][:2] == pairs[i][:2]:
+                j += 1
+            chunk = [q[2] for q in pairs[i:j]]
+            while len(chunk) % BM:
+                chunk.append(P)
+            rows += chunk
+            te += [pairs[i][0]] * (len(chunk) // BM)
+            tl += [pairs[i][1]] * (len(chunk) // BM)
+            i = j
+        n = len(rows)
+        assert out["sorted_pair_ids"][:n].tolist() == rows
+        assert out["tile_expert"][:n // BM].tolist() == te
+        assert out["tile_lora"][:n // BM].tolist() == tl
+        offs = [next((ti for ti, ee in enumerate(te) if ee >= e), len(te)) for e in range(E)] + [len(te)]
+        assert out["expert_tile_offsets"].tolist() == offs
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+def _torch_peft_reference(inp, enabled, mapping):
+    """The layer built from torch.nn.functional pieces, PEFT style: for each
+    pair, base linear + scaling * lora_B(lora_A(x)) with lora_A.weight = A
+    [r, in] and lora_B.weight = B [out, r] (the pool stores B^T)."""
+    T, k = inp["topk_ids"].shape
+    x = torch.from_numpy(inp["x"])
+    wgu = torch.from_numpy(inp["w_gate_up"])
+    wd = torch.from_numpy(inp["w_down"])
+    I = wgu.shape[1] // 2
+    y = torch.zeros_like(x)
+    have = "a_gate" in inp
+    for t in range(T):
+        for j in range(k):
+            e = int(inp["topk_ids"][t, j])
+            l = int(mapping[t])
+            on = have and l >= 0 and enabled[l] == 1 and inp["lora_ranks"][l] > 0
+
+            def lin(v, W, A=None, B=None):
+                out = F.linear(v, W)
+                if on:
+                    r, s = int(inp["lora_ranks"][l]), float(inp["scaling"][l])
+                    A_w = torch.from_numpy(A[l, e, :r])
+                    B_w = torch.from_numpy(B[l, e, :r]).T.contiguous()
+                    out = out + s * F.linear(F.linear(v, A_w), B_w)
+                return out
+            xv = x[t]
+            g = lin(xv, wgu[e, :I], inp.get("a_gate"), inp.get("b_gate"))
+            u = lin(xv, wgu[e, I:], inp.get("a_up"), inp.get("b_up"))
+            a = F.silu(g) * u
+            z = lin(a, wd[e], inp.get("a_down"), inp.get("b_down"))
+            y[t] += float(inp["topk_weights"][t, j]) * z
+    return y.numpy()
+
+
+def pin_forward_torch_layers(orc):
+    for spec in (tiny_spec(1), tiny_spec(2, top_k=1, num_experts=1),
+                 tiny_spec(3, num_loras=0, lora_ranks=[], weight_indices=[-1, -1, -1, -1])):
+        inp = np_inputs(spec)
+        en, mp = info_of(orc, inp)
+        ref = _torch_peft_reference(inp, en, mp)
+        for fn in ("moe_lora_forward", "moe_lora_forward_bruteforce"):
+            got = fwd(orc, inp, fn)
+            assert rel_l2(got, ref) < 1e-12, (fn, rel_l2(got, ref))
+
+
+def pin_forward_config0_bruteforce(orc):
+    inp = np_inputs(workloads.config("c0"))
+    a = fwd(orc, inp, "moe_lora_forward")
+    b = fwd(orc, inp, "moe_lora_forward_bruteforce")
+    assert np.all(np.isfinite(a))
+    assert rel_l2(a, b) < 1e-12
+    en, mp = info_of(orc, inp)
+    ref = _torch_peft_reference(inp, en, mp)
+    assert rel_l2(a, ref) < 1e-12
+
+
+def pin_forward_random_bruteforce(orc):
+    rng = np.random.default_rng(3)
+    for i in range(12):
+        spec = workloads.random_spec(rng, name=f"r{i}")
+        inp = np_inputs(spec)
+        a = fwd(orc, inp, "moe_lora_forward")
+        b = fwd(orc, inp, "moe_lora_forward_bruteforce")
+        assert np.all(np.isfinite(a))
+        assert rel_l2(a, b) < 1e-11 or np.linalg.norm(b) == 0
+
+
+def pin_forward_reduces_to_base(orc):
+    spec = tiny_spec(4)
+    inp = np_inputs(spec)
+    base = fwd(orc, inp, lora=False)
+    # B = 0 everywhere
+    zero_b = {n: np.zeros_like(inp[n]) for n in ("b_gate", "b_up", "b_down")}
+    assert np.array_equal(fwd(orc, inp, **zero_b), base)
+    # all ranks zero
+    assert np.array_equal(fwd(orc, inp, lora_ranks=np.zeros_like(inp["lora_ranks"])), base)
+    # every token maps to -1
+    en, mp = info_of(orc, inp)
+    assert np.array_equal(fwd(orc, inp, token_lora_mapping=np.full_like(mp, -1)), base)
+    # all slots disabled
+    assert np.array_equal(fwd(orc, inp, adapter_enabled=np.zeros_like(en)), base)
+    # LoRA does change the output when on
+    assert not np.allclose(fwd(orc, inp), base)
+
+
+def pin_forward_merged_weights(orc):
+    """LoRA on == base layer run with W' = W + s * B A for a single slot."""
+    spec = tiny_spec(5, seg_lens=[4, 3], weight_indices=[0, 0], lora_ranks=[5, 0, 3])
+    inp = np_inputs(spec)
+    l, r, s = 0, 5, float(inp["scaling"][0])
+    I = spec.inter
+    wgu = inp["w_gate_up"].copy()
+    wd = inp["w_down"].copy()
+    for e in range(spec.num_experts):
+        wgu[e, :I] += s * inp["b_gate"][l, e, :r].T @ inp["a_gate"][l, e, :r]
+        wgu[e, I:] += s * inp["b_up"][l, e, :r].T @ inp["a_up"][l, e, :r]
+        wd[e] += s * inp["b_down"][l, e, :r].T @ inp["a_down"][l, e, :r]
+    merged = fwd(orc, inp, lora=False, w_gate_up=wgu, w_down=wd)
+    assert rel_l2(fwd(orc, inp), merged) < 1e-12
+
+
+def pin_forward_down_linear_in_bd(orc):
+    inp = np_inputs(tiny_spec(6))
+    y0 = fwd(orc, inp, b_down=np.zeros_like(inp["b_down"]))
+    y1 = fwd(orc, inp)
+    c = 3.0
+    yc = fwd(orc, inp, b_down=c * inp["b_down"])
+    assert rel_l2(yc - y0, c * (y1 - y0)) < 1e-10
+
+
+def pin_forward_permutations(orc):
+    spec = tiny_spec(7)
+    inp = np_inputs(spec)
+    y = fwd(orc, inp)
+    # permute top-k slots (ids and weights together)
+    k = spec.top_k
+    perm = np.arange(k)[::-1]
+    y2 = fwd(orc, inp, topk_ids=inp["topk_ids"][:, perm], topk_weights=inp["topk_weights"][:, perm])
+    assert rel_l2(y2, y) < 1e-13
+    # permute requests with their tokens
+    m = inp["meta"]
+    indptr = m["seg_indptr"]
+    bs = len(indptr) - 1
+    rp = np.arange(bs)[::-1]
+    tok = np.concatenate([np.arange(indptr[b], indptr[b + 1]) for b in rp]).astype(np.int64)
+    lens = np.diff(indptr)[rp]
+    indptr2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    wi2 = m["weight_indices"][rp]
+    en2, mp2 = orc.moe_lora_info(len(tok), indptr2, wi2, m["lora_ranks"], 0)
+    y3 = fwd(orc, inp, x=inp["x"][tok], topk_ids=inp["topk_ids"][tok],
+             topk_weights=inp["topk_weights"][tok], token_lora_mapping=mp2, adapter_enabled=en2)
+    assert rel_l2(y3, y[tok]) < 1e-13
+
+
+def pin_forward_identical_experts(orc):
+    spec = tiny_spec(8, lora_ranks=[4, 0, 6])
+    inp = np_inputs(spec)
+    E = spec.num_experts
+    wgu = np.repeat(inp["w_gate_up"][:1], E, axis=0)
+    wd = np.repeat(inp["w_down"][:1], E, axis=0)
+    pools = {n: np.repeat(inp[n][:, :1], E, axis=1) for n in
+             ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")}
+    y_all = fwd(orc, inp, w_gate_up=wgu, w_down=wd, **pools)
+    ids1 = np.zeros((spec.num_tokens, 1), np.int32)
+    w1 = np.ones((spec.num_tokens, 1), np.float64)
+    y_one = fwd(orc, inp, w_gate_up=wgu, w_down=wd, topk_ids=ids1, topk_weights=w1, **pools)
+    # router weights are renormalised to sum to 1 over the top-k
+    assert rel_l2(y_all, y_one) < 1e-6
+
+
+def pin_forward_token_subset(orc):
+    inp = np_inputs(tiny_spec(9))
+    y = fwd(orc, inp)
+    sub = [5, 0, 3]
+    ys = fwd(orc, inp, tokens=sub)
+    assert rel_l2(ys, y[sub]) < 1e-14
+
+
+def pin_silu(orc):
+    from scipy.special import expit
+    v = np.linspace(-40, 40, 2001)
+    assert np.allclose(orc.silu(v), v * expit(v), rtol=1e-14, atol=1e-300)
+    assert orc.silu(np.array([0.0]))[0] == 0.0
+    ref = F.silu(torch.from_numpy(v)).numpy()
+    assert np.allclose(orc.silu(v), ref, rtol=1e-13, atol=1e-300)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
