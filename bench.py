@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert layer with per-request LoRA deltas on one MI355X.
+
+A step is one pass of the whole hot path over one batch: moe_lora_info (the
+per-batch metadata), moe_lora_align and moe_lora_forward, on the Mixtral-shaped
+prefill workload (8 experts, top-2, hidden 4096, intermediate 14336, 4096
+tokens in 16 requests, 8 adapter slots of rank 16, bf16) unless --config says
+otherwise.  Inputs are synthetic and resident in HBM before timing starts.
+
+Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
+gate_up GEMM, timed with HIP events around its launch inside the timed region)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector / MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through libamdhip64 (recorded by the library on
+    the stream its kernels run on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def counts(spec, meta):
+    """FLOPs and bytes the method itself must do for this batch (padding,
+    intermediates and pool rows beyond each slot's rank excluded)."""
+    T, k, E, H, I = spec.num_tokens, spec.top_k, spec.num_experts, spec.hidden, spec.inter
+    ids = meta["topk_ids"]
+    indptr = meta["seg_indptr"]
+    wi = meta["weight_indices"]
+    ranks = meta["lora_ranks"]
+    mapping = np.repeat(wi, np.diff(indptr))
+    used = set(int(v) for v in wi if v >= 0)
+    on_slot = np.array([(l in used and ranks[l] > 0) for l in range(len(ranks))], dtype=bool)
+    tok = np.repeat(np.arange(T), k)
+    e_of = ids.reshape(-1)
+    l_of = mapping[tok]
+    r_of = np.where((l_of >= 0) & on_slot[np.maximum(l_of, 0)] if len(ranks) else False,
+                    ranks[np.maximum(l_of, 0)] if len(ranks) else 0, 0)
+    P = T * k
+    esz = 2 if spec.dtype == "bf16" else 4
+    fl_gate_up_base = 4.0 * H * I * P
+    fl_gate_up_expand = 4.0 * float(np.sum(r_of)) * I
+    fl_shrink = 4.0 * float(np.sum(r_of)) * H + 2.0 * float(np.sum(r_of)) * I
+    fl_down = 2.0 * H * I * P + 2.0 * float(np.sum(r_of)) * H
+    total_flops = fl_gate_up_base + fl_gate_up_expand + fl_shrink + fl_down
+    active = np.unique(e_of)
+    w_bytes = len(active) * 3.0 * H * I * esz
+    buckets = set(zip(e_of[r_of > 0].tolist(), l_of[r_of > 0].tolist()))
+    lora_bytes = sum(3.0 * ranks[l] * (H + I) * esz for (_, l) in buckets)
+    io_bytes = 2.0 * T * H * esz + 8.0 * P
+    gate_up_bytes = len(active) * 2.0 * H * I * esz + T * H * esz
+    return dict(total_flops=total_flops, gate_up_flops=fl_gate_up_base + fl_gate_up_expand,
+                total_bytes=w_bytes + lora_bytes + io_bytes, gate_up_bytes=gate_up_bytes,
+                active_experts=int(len(active)), lora_buckets=len(buckets))
+
+
+def cpu_baseline(spec, inp, n_tokens):
+    """The oracle as it stands, on a bounded sample of the workload's tokens."""
+    import oracle
+    import torch
+
+    T = spec.num_tokens
+    sample = np.unique(np.linspace(0, T - 1, min(n_tokens, T)).astype(np.int64))
+    m = inp["meta"]
+
+    class View:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, idx):
+            idx = idx if isinstance(idx, tuple) else (idx,)
+            return self.t[tuple(int(i) for i in idx)].float().cpu().numpy()
+
+    x_host = inp["x"][torch.as_tensor(sample, device=inp["x"].device)].float().cpu().numpy()
+    # the oracle indexes x by token id; give it a dict view over the sample
+    xs = {int(t): x_host[i] for i, t in enumerate(sample)}
+
+    class XView:
+        def __getitem__(self, t):
+            return xs[int(t)]
+
+    pools = {n: View(inp[n]) for n in ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
+             if n in inp}
+    t0 = time.perf_counter()
+    en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
+                                  m["max_seg_len"])
+    oracle.moe_lora_forward(XView(), m["topk_ids"], m["topk_weights"], View(inp["w_gate_up"]),
+                            View(inp["w_down"]), m["lora_ranks"], m["scaling"], mp, en,
+                            tokens=sample, **pools)
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return dict(value=len(sample) / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{len(sample)} of {T} tokens (evenly spaced) of the same batch; float64 "
+                       f"numpy oracle incl. per-expert upcast of the touched weights; {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer is TP=1 on a single MI355X and this build "
+              "has no multi-GPU path (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_expert_layer_segment_amd import binding, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = workloads.config(args.config)
+    print(f"[bench] generating {spec.name} on {dev}", file=sys.stderr, flush=True)
+    inp = workloads.generate(spec, device=dev, canary=False)
+    torch.cuda.synchronize()
+
+    T, k, E = spec.num_tokens, spec.top_k, spec.num_experts
+    L = spec.num_loras
+    BM = 16
+    pools = {n: inp[n] for n in binding._POOLS} if L > 0 else None
+    en_buf = torch.empty(max(L, 1), dtype=torch.int32, device=dev)
+    mp_buf = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    en, mp = binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
+                                   en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+    al = binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, E, L, BM)
+    al_ws = torch.empty(binding.moe_lora_align_workspace_bytes(T, k, E, L, BM), dtype=torch.uint8,
+                        device=dev)
+    y = torch.empty_like(inp["x"])
+    fws = torch.empty(binding.moe_lora_forward_workspace_bytes(
+        inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"], al, k,
+        inp["lora_ranks"], inp["scaling"], pools), dtype=torch.uint8, device=dev)
+
+    hip = HipEvents()
+    nst = len(binding.FORWARD_STAGES)
+
+    def step(events=None):
+        binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
+                              en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+        binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, E, L, BM, out=al,
+                               workspace=al_ws)
+        binding.moe_lora_forward(inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"],
+                                 al, k, inp["lora_ranks"] if L > 0 else None,
+                                 inp["scaling"] if L > 0 else None, pools, y=y, workspace=fws,
+                                 events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = [hip.create(2 * nst) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(ev[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in ev]))
+                for i, name in enumerate(binding.FORWARD_STAGES)}
+    for e in ev:
+        hip.destroy(e)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)",
+          file=sys.stderr, flush=True)
+
+    c = counts(spec, inp["meta"])
+    gu_ms = stage_ms["gate_up_gemm"]
+    achieved = c["gate_up_flops"] / (gu_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_FP32_TFLOPS
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f).get(spec.name, {}).get("gate_up_gemm")
+        if tr:
+            traffic = tr
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic,
+                    kernel="gate_up_gemm", kernel_ms=round(gu_ms, 4),
+                    kernel_flops=c["gate_up_flops"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, inp, args.cpu_sample_tokens)
+
+    tok_s = T / (ms * 1e-3)
+    out = {
+        "metric": "MoE-LoRA layer tokens/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "experts": E, "top_k": k, "hidden": spec.hidden,
+                   "intermediate": spec.inter, "tokens": T, "requests": spec.num_reqs,
+                   "adapter_slots": L, "lora_ranks": list(spec.lora_ranks),
+                   "block_m": BM, "parallelism": "tp1"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "layer": {"tflops": round(c["total_flops"] / (ms * 1e-3) / 1e12, 2),
+                  "gbs": round(c["total_bytes"] / (ms * 1e-3) / 1e9, 1),
+                  "algorithmic_flops": c["total_flops"], "algorithmic_bytes": c["total_bytes"],
+                  "active_experts": c["active_experts"], "lora_buckets": c["lora_buckets"]},
+        "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * moe_lora.h -- C ABI of the MI355X (gfx950) MoE expert layer with per-request
+ * LoRA deltas.
+ *
+ * The layer (SGLang PR #14105 page, "LoRA on MoE expert layers", section
+ * 实现拆解, the layer formula) computes, for every token t with top-k experts
+ * e_j and router weights w_j, and the token's adapter slot l:
+ *
+ *   y_t = sum_j w_j * (W_down[e] + s_l B_d A_d)
+ *                     [ SiLU((W_gate[e] + s_l B_g A_g) x_t) * ((W_up[e] + s_l B_u A_u) x_t) ]
+ *
+ * with LoRA factors taken from 4-D pools [num_loras, num_experts, rank, dim]
+ * (same page, same section) and the slot picked per token from request
+ * segments (SGLang PR #24160 page, "shared MoE LoRA batch info", sections
+ * 实现拆解 and 关键源码片段).
+ *
+ * Three calls:
+ *   moe_lora_info    -- once per batch: token_lora_mapping and adapter_enabled.
+ *   moe_lora_align   -- per layer: bucket (token, expert) pairs by (expert, adapter),
+ *                       padded to block_m rows.
+ *   moe_lora_forward -- per layer: grouped gate_up GEMM with fused LoRA expand and
+ *                       SiLU*mul, grouped down GEMM with fused LoRA expand and the
+ *                       router weight, then the top-k combine.
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or retains memory.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) with no host synchronisation.
+ *   - Validation reads host scalars only; device contents are never read on the
+ *     host.  Calls on disjoint buffers may run concurrently.
+ *   - Integer metadata is int32; router weights and scaling are float32.
+ *   - Return value: MOE_LORA_OK or one of the negative codes below.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_LORA_OK = 0,
+  MOE_LORA_ERR_INVALID = -1,     /* null pointer, bad dimension or inconsistent sizes */
+  MOE_LORA_ERR_UNDERCOVER = -2,  /* num_reqs * max_seg_len < num_tokens (info only)   */
+  MOE_LORA_ERR_UNSUPPORTED = -3, /* dtype or size outside what the kernels support     */
+  MOE_LORA_ERR_HIP = -4,         /* a HIP launch / runtime error                        */
+  MOE_LORA_ERR_WORKSPACE = -5    /* workspace missing or too small                      */
+};
+
+typedef enum { MOE_LORA_F32 = 0, MOE_LORA_BF16 = 1 } moe_lora_dtype;
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* moe_lora_status_str(int status);
+
+/*
+ * moe_lora_info -- per-batch MoE-LoRA metadata (SGLang PR #24160 page,
+ * section 实现拆解 items 1-3; its unit test in section 关键源码片段).
+ *
+ *   seg_indptr      [num_reqs + 1]  request segments: request b owns tokens
+ *                                   [seg_indptr[b], seg_indptr[b+1]); must start at
+ *                                   0, be nondecreasing and end at num_tokens.
+ *   weight_indices  [num_reqs]      slot of each request (req_to_lora), -1 = none.
+ *   lora_ranks      [num_loras]     rank of each slot, >= 0.
+ *   adapter_enabled [num_loras] out 1 iff some request names the slot and its rank
+ *                                   is > 0, else 0.  Every entry is written.
+ *   token_lora_mapping [>= num_tokens] out  weight_indices repeated over each
+ *                                   segment (-1 kept).  Entries past num_tokens are
+ *                                   left untouched.
+ *   max_seg_len     host hint of the longest segment; when > 0 and
+ *                   num_reqs * max_seg_len < num_tokens the call returns
+ *                   MOE_LORA_ERR_UNDERCOVER ("under-covers tokens") and launches
+ *                   nothing.  0 skips the check.  The kernel itself covers every
+ *                   token whatever the hint.
+ * num_tokens == 0 is valid (only adapter_enabled is written).  num_loras == 0 is
+ * valid.  Out-of-range device values (weight_indices outside [-1, num_loras)) are
+ * ignored for adapter_enabled and copied through to the mapping.
+ */
+int moe_lora_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras, int32_t max_seg_len,
+                  const int32_t* seg_indptr, const int32_t* weight_indices,
+                  const int32_t* lora_ranks, int32_t* adapter_enabled,
+                  int32_t* token_lora_mapping, void* stream);
+
+/*
+ * Capacity (rows) of the align outputs: P + min(P, E*(L+1)) * (block_m - 1)
+ * rounded up to block_m, with P = num_tokens * top_k.  sorted_pair_ids needs
+ * this many entries; tile_expert / tile_lora need capacity / block_m.
+ * Returns -1 for invalid arguments.
+ */
+int64_t moe_lora_align_capacity_rows(int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                                     int32_t num_loras, int32_t block_m);
+
+/* Workspace bytes moe_lora_align needs for these sizes (0 on invalid arguments). */
+size_t moe_lora_align_workspace_bytes(int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                                      int32_t num_loras, int32_t block_m);
+
+/*
+ * moe_lora_align -- bucket (token, expert) pairs by expert and adapter (SGLang
+ * PR #14105 page, section 实现拆解: tokens sorted by LoRA adapter and expert id).
+ *
+ * Pair p = t * top_k + j has expert e = topk_ids[t * top_k + j] and effective
+ * slot a = token_lora_mapping[t] if that is >= 0 and adapter_enabled[it] == 1,
+ * else -1 (so rank-0 and unused slots fall into the no-LoRA bucket).  Buckets are
+ * ordered by key e * (num_loras + 1) + (a + 1) (expert-major, no-LoRA first);
+ * inside a bucket pairs keep ascending p.  Each bucket is padded with the
+ * sentinel P = num_tokens * top_k up to a multiple of block_m rows; every
+ * block_m rows form one tile.
+ *
+ *   topk_ids            [num_tokens, top_k]   expert ids in [0, num_experts).
+ *   token_lora_mapping  [num_tokens]          from moe_lora_info.
+ *   adapter_enabled     [num_loras]           from moe_lora_info (may be NULL iff
+ *                                              num_loras == 0).
+ *   sorted_pair_ids     [capacity]      out   pair ids in bucket order; P for pads
+ *                                              and for the unused tail.
+ *   tile_expert         [capacity/block_m] out expert of each tile, -1 past the end.
+ *   tile_lora           [capacity/block_m] out effective slot of each tile (-1 = no
+ *                                              LoRA, and past the end).
+ *   expert_tile_offsets [num_experts + 1] out  first tile of each expert (experts
+ *                                              with no pairs repeat the next
+ *                                              offset); [num_experts] = tile count.
+ *   num_rows_padded     [1]             out   tiles * block_m.
+ *   workspace           >= moe_lora_align_workspace_bytes(...) bytes of device memory.
+ * block_m must be a multiple of 16 in [16, 256].  Supports
+ * num_experts * (num_loras + 1) <= 32768.  Expert ids outside [0, num_experts)
+ * are undefined input; they never cause out-of-bounds writes.
+ * Every output word up to the capacity is written, so results are fully defined.
+ */
+int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32_t num_loras,
+                   int32_t block_m, const int32_t* topk_ids, const int32_t* token_lora_mapping,
+                   const int32_t* adapter_enabled, int32_t* sorted_pair_ids, int32_t* tile_expert,
+                   int32_t* tile_lora, int32_t* expert_tile_offsets, int32_t* num_rows_padded,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Arguments of moe_lora_forward.  All tensors are row-major and contiguous.
+ * `dtype` applies to x, the expert weights, the six pools and y.
+ *
+ *   x            [T, H]           hidden states.
+ *   topk_ids     [T, k] int32     (only used through the align outputs; may be NULL).
+ *   topk_weights [T, k] float32   router weights, applied to each expert output.
+ *   w_gate_up    [E, 2I, H]       rows [0, I) = gate, rows [I, 2I) = up (nn.Linear
+ *                                  [out, in] layout stacked over experts).
+ *   w_down       [E, H, I]
+ *   a_gate, a_up [L, E, R, H]     LoRA A of gate / up, rank-major.
+ *   b_gate, b_up [L, E, R, I]     LoRA B of gate / up stored transposed (rank-major).
+ *   a_down       [L, E, R, I]
+ *   b_down       [L, E, R, H]     LoRA B of down, transposed.
+ *   lora_ranks   [L] int32        rows >= lora_ranks[l] of slot l's pools are never read.
+ *   scaling      [L] float32      s_l = alpha / r of each slot.
+ *   sorted_pair_ids, tile_expert, tile_lora, expert_tile_offsets, num_rows_padded:
+ *                the outputs of moe_lora_align for the same topk_ids, mapping,
+ *                block_m.  Any layout with the same structure works (every pair
+ *                exactly once, tiles uniform in (expert, slot), each expert's tiles
+ *                contiguous and listed by expert_tile_offsets).
+ *   workspace    >= moe_lora_forward_workspace_bytes(args) bytes of device memory.
+ *   y            [T, H] out       overwritten.
+ * num_loras == 0 (pools NULL) runs the plain MoE layer.  H and I must be
+ * multiples of 64, R <= 64, top_k <= num_experts.
+ */
+typedef struct moe_lora_forward_args {
+  size_t struct_size; /* sizeof(moe_lora_forward_args) */
+  int32_t dtype;      /* moe_lora_dtype */
+  int32_t num_tokens, hidden, inter, num_experts, top_k, num_loras, max_rank, block_m;
+  const void* x;
+  const int32_t* topk_ids;
+  const float* topk_weights;
+  const void* w_gate_up;
+  const void* w_down;
+  const void* a_gate;
+  const void* a_up;
+  const void* b_gate;
+  const void* b_up;
+  const void* a_down;
+  const void* b_down;
+  const int32_t* lora_ranks;
+  const float* scaling;
+  const int32_t* sorted_pair_ids;
+  const int32_t* tile_expert;
+  const int32_t* tile_lora;
+  const int32_t* expert_tile_offsets;
+  const int32_t* num_rows_padded;
+  void* workspace;
+  size_t workspace_bytes;
+  void* y;
+} moe_lora_forward_args;
+
+/* Workspace bytes moe_lora_forward needs for the sizes in `args` (0 if invalid). */
+size_t moe_lora_forward_workspace_bytes(const moe_lora_forward_args* args);
+
+/*
+ * moe_lora_forward -- the layer (SGLang PR #14105 page, section 实现拆解): gate/up
+ * projections with LoRA, SiLU(gate) * up, down projection with LoRA, router
+ * weight, and the sum over the top-k experts (in slot order j = 0..k-1, fp32).
+ */
+int moe_lora_forward(const moe_lora_forward_args* args, void* stream);
+
+/*
+ * Number of kernel stages of moe_lora_forward, in launch order: 0 plan (work
+ * items), 1 gate/up LoRA shrink, 2 gate_up GEMM (+LoRA expand, SiLU*mul),
+ * 3 down LoRA shrink, 4 down GEMM (+LoRA expand, router weight), 5 top-k combine.
+ */
+#define MOE_LORA_FORWARD_STAGES 6
+
+/*
+ * moe_lora_forward_events -- moe_lora_forward for measurement: additionally
+ * records the caller's hipEvent_t handles on `stream`, events[2s] before and
+ * events[2s+1] after stage s (s < MOE_LORA_FORWARD_STAGES; NULL entries are
+ * skipped; a stage that launches nothing gets two adjacent records).  Adds no
+ * synchronisation; results are identical to moe_lora_forward.  The caller owns
+ * the events and reads them with hipEventElapsedTime after synchronising.
+ */
+int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
+                            void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

@@ -1,0 +1,323 @@
+"""ctypes binding of the gfx950 MoE-LoRA library (argument marshalling only).
+
+Every step of the layer runs in the HIP kernels behind ``include/moe_lora.h``;
+this module only checks tensor shapes / dtypes / devices, allocates outputs and
+workspaces with PyTorch, and passes raw device pointers and the current HIP
+stream.  If the shared library is missing it raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_lora.so")
+
+OK, ERR_INVALID, ERR_UNDERCOVER, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
+DTYPE_F32, DTYPE_BF16 = 0, 1
+FORWARD_STAGES = ("plan", "shrink_gate_up", "gate_up_gemm", "shrink_down", "down_gemm", "combine")
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class ForwardArgs(ctypes.Structure):
+    """Mirror of ``moe_lora_forward_args``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("dtype", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("num_loras", ctypes.c_int32),
+        ("max_rank", ctypes.c_int32), ("block_m", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+        ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("a_gate", ctypes.c_void_p), ("a_up", ctypes.c_void_p), ("b_gate", ctypes.c_void_p),
+        ("b_up", ctypes.c_void_p), ("a_down", ctypes.c_void_p), ("b_down", ctypes.c_void_p),
+        ("lora_ranks", ctypes.c_void_p), ("scaling", ctypes.c_void_p),
+        ("sorted_pair_ids", ctypes.c_void_p), ("tile_expert", ctypes.c_void_p),
+        ("tile_lora", ctypes.c_void_p), ("expert_tile_offsets", ctypes.c_void_p),
+        ("num_rows_padded", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("y", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"MoE-LoRA HIP library not found at {LIB_PATH}; build it with "
+            "`python -m moe_expert_layer_segment_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.moe_lora_status_str.restype = ctypes.c_char_p
+    L.moe_lora_status_str.argtypes = [ctypes.c_int]
+    L.moe_lora_info.restype = ctypes.c_int
+    L.moe_lora_info.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 6
+    L.moe_lora_align_capacity_rows.restype = ctypes.c_int64
+    L.moe_lora_align_capacity_rows.argtypes = [ctypes.c_int32] * 5
+    L.moe_lora_align_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_lora_align_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+    L.moe_lora_align.restype = ctypes.c_int
+    L.moe_lora_align.argtypes = ([ctypes.c_int32] * 5 + [ctypes.c_void_p] * 9 +
+                                 [ctypes.c_size_t, ctypes.c_void_p])
+    L.moe_lora_forward_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_lora_forward_workspace_bytes.argtypes = [ctypes.POINTER(ForwardArgs)]
+    L.moe_lora_forward.restype = ctypes.c_int
+    L.moe_lora_forward.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.c_void_p]
+    L.moe_lora_forward_events.restype = ctypes.c_int
+    L.moe_lora_forward_events.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p)]
+    _LIB = L
+    return L
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().moe_lora_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status == ERR_UNDERCOVER:
+        # the pages' unit test expects an AssertionError naming under-coverage
+        raise AssertionError(f"{where}: launch under-covers tokens")
+    if status != OK:
+        raise MoeLoraError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+
+
+# ---------------------------------------------------------------------------
+# info
+# ---------------------------------------------------------------------------
+def moe_lora_info(num_tokens: int, seg_indptr: torch.Tensor, lora_ranks: torch.Tensor,
+                  weight_indices: torch.Tensor, adapter_enabled: Optional[torch.Tensor] = None,
+                  token_lora_mapping: Optional[torch.Tensor] = None, max_len: int = 0):
+    """Per-batch metadata; returns (adapter_enabled, token_lora_mapping[:num_tokens]).
+
+    Argument order follows the pages' ``_compute_moe_lora_info``.  Preallocated
+    outputs are written in place and returned as views of the same storage.
+    Raises AssertionError when num_reqs * max_len < num_tokens.
+    """
+    dev = seg_indptr.device
+    num_reqs = seg_indptr.numel() - 1
+    num_loras = lora_ranks.numel()
+    _need(seg_indptr, "seg_indptr", torch.int32)
+    _need(lora_ranks, "lora_ranks", torch.int32, dev)
+    _need(weight_indices, "weight_indices", torch.int32, dev, num_reqs)
+    if adapter_enabled is None:
+        adapter_enabled = torch.empty(num_loras, dtype=torch.int32, device=dev)
+    if token_lora_mapping is None:
+        token_lora_mapping = torch.empty(max(num_tokens, 1), dtype=torch.int32, device=dev)
+    _need(adapter_enabled, "adapter_enabled", torch.int32, dev, num_loras)
+    _need(token_lora_mapping, "token_lora_mapping", torch.int32, dev, num_tokens)
+    st = lib().moe_lora_info(num_tokens, num_reqs, num_loras, int(max_len), _ptr(seg_indptr),
+                             _ptr(weight_indices), _ptr(lora_ranks), _ptr(adapter_enabled),
+                             _ptr(token_lora_mapping), _stream())
+    _check(st, "moe_lora_info")
+    return adapter_enabled, token_lora_mapping[:num_tokens]
+
+
+compute_moe_lora_info = moe_lora_info
+
+
+# ---------------------------------------------------------------------------
+# align
+# ---------------------------------------------------------------------------
+def moe_lora_align_capacity_rows(num_tokens, top_k, num_experts, num_loras, block_m) -> int:
+    v = lib().moe_lora_align_capacity_rows(num_tokens, top_k, num_experts, num_loras, block_m)
+    if v < 0:
+        raise MoeLoraError(ERR_INVALID, "moe_lora_align_capacity_rows")
+    return int(v)
+
+
+def moe_lora_align_workspace_bytes(num_tokens, top_k, num_experts, num_loras, block_m) -> int:
+    return int(lib().moe_lora_align_workspace_bytes(num_tokens, top_k, num_experts, num_loras,
+                                                    block_m))
+
+
+def moe_lora_align(topk_ids: torch.Tensor, token_lora_mapping: torch.Tensor,
+                   adapter_enabled: Optional[torch.Tensor], num_experts: int, num_loras: int,
+                   block_m: int = 16, out: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Bucket (token, expert) pairs by (expert, adapter); returns the align outputs."""
+    dev = topk_ids.device
+    T, k = topk_ids.shape
+    _need(topk_ids, "topk_ids", torch.int32)
+    _need(token_lora_mapping, "token_lora_mapping", torch.int32, dev, T)
+    if num_loras > 0:
+        _need(adapter_enabled, "adapter_enabled", torch.int32, dev, num_loras)
+    cap = moe_lora_align_capacity_rows(T, k, num_experts, num_loras, block_m)
+    if out is None:
+        out = dict(
+            sorted_pair_ids=torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+            tile_expert=torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+            tile_lora=torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+            expert_tile_offsets=torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+            num_rows_padded=torch.empty(1, dtype=torch.int32, device=dev))
+    for name, n in (("sorted_pair_ids", cap), ("tile_expert", cap // block_m),
+                    ("tile_lora", cap // block_m), ("expert_tile_offsets", num_experts + 1),
+                    ("num_rows_padded", 1)):
+        _need(out[name], name, torch.int32, dev, n)
+    wsb = moe_lora_align_workspace_bytes(T, k, num_experts, num_loras, block_m)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev, wsb)
+    st = lib().moe_lora_align(T, k, num_experts, num_loras, block_m, _ptr(topk_ids),
+                              _ptr(token_lora_mapping),
+                              _ptr(adapter_enabled) if num_loras > 0 else None,
+                              _ptr(out["sorted_pair_ids"]), _ptr(out["tile_expert"]),
+                              _ptr(out["tile_lora"]), _ptr(out["expert_tile_offsets"]),
+                              _ptr(out["num_rows_padded"]), _ptr(workspace), workspace.numel(),
+                              _stream())
+    _check(st, "moe_lora_align")
+    out["capacity"] = cap
+    out["block_m"] = block_m
+    return out
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+_POOLS = ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
+
+
+def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
+                  top_k, y, workspace) -> ForwardArgs:
+    T, H = x.shape
+    E, twoI, H2 = w_gate_up.shape
+    I = twoI // 2
+    if x.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    dev = x.device
+    _need(x, "x", x.dtype)
+    _need(w_gate_up, "w_gate_up", x.dtype, dev)
+    _need(w_down, "w_down", x.dtype, dev)
+    if H2 != H or tuple(w_down.shape) != (E, H, I):
+        raise ValueError("weight shapes do not match x / each other")
+    _need(topk_weights, "topk_weights", torch.float32, dev, T * top_k)
+    L, R = 0, 0
+    if pools is not None:
+        L, E2, R, _ = pools["a_gate"].shape
+        if E2 != E:
+            raise ValueError("pool expert axis does not match the weights")
+        shapes = dict(a_gate=(L, E, R, H), a_up=(L, E, R, H), b_gate=(L, E, R, I),
+                      b_up=(L, E, R, I), a_down=(L, E, R, I), b_down=(L, E, R, H))
+        for n in _POOLS:
+            _need(pools[n], n, x.dtype, dev)
+            if tuple(pools[n].shape) != shapes[n]:
+                raise ValueError(f"{n} must have shape {shapes[n]}, got {tuple(pools[n].shape)}")
+        _need(lora_ranks, "lora_ranks", torch.int32, dev, L)
+        _need(scaling, "scaling", torch.float32, dev, L)
+    a = ForwardArgs()
+    a.struct_size = ctypes.sizeof(ForwardArgs)
+    a.dtype = dt
+    a.num_tokens, a.hidden, a.inter, a.num_experts, a.top_k = T, H, I, E, top_k
+    a.num_loras, a.max_rank, a.block_m = L, R, int(align_out["block_m"])
+    a.x, a.topk_weights = x.data_ptr(), topk_weights.data_ptr()
+    a.w_gate_up, a.w_down = w_gate_up.data_ptr(), w_down.data_ptr()
+    if pools is not None:
+        for n in _POOLS:
+            setattr(a, n, pools[n].data_ptr())
+        a.lora_ranks, a.scaling = lora_ranks.data_ptr(), scaling.data_ptr()
+    for n in ("sorted_pair_ids", "tile_expert", "tile_lora", "expert_tile_offsets",
+              "num_rows_padded"):
+        _need(align_out[n], n, torch.int32, dev)
+        setattr(a, n, align_out[n].data_ptr())
+    if y is not None:
+        _need(y, "y", x.dtype, dev, T * H)
+        a.y = y.data_ptr()
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return a
+
+
+def moe_lora_forward_workspace_bytes(x, topk_weights, w_gate_up, w_down, align_out, top_k,
+                                     lora_ranks=None, scaling=None, pools=None) -> int:
+    a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
+                      top_k, None, None)
+    n = int(lib().moe_lora_forward_workspace_bytes(ctypes.byref(a)))
+    if n == 0:
+        raise MoeLoraError(ERR_INVALID, "moe_lora_forward_workspace_bytes")
+    return n
+
+
+def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: torch.Tensor,
+                     w_down: torch.Tensor, align_out: Dict[str, torch.Tensor], top_k: int,
+                     lora_ranks: Optional[torch.Tensor] = None,
+                     scaling: Optional[torch.Tensor] = None,
+                     pools: Optional[Dict[str, torch.Tensor]] = None,
+                     y: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     events=None) -> torch.Tensor:
+    """The MoE-LoRA layer: returns y [T, H] (written into ``y`` if given).
+
+    ``events``: optional sequence of 2 * len(FORWARD_STAGES) raw hipEvent_t
+    handles recorded around each kernel stage (measurement only).
+    """
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        n = moe_lora_forward_workspace_bytes(x, topk_weights, w_gate_up, w_down, align_out, top_k,
+                                             lora_ranks, scaling, pools)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
+                      top_k, y, workspace)
+    if events is None:
+        _check(lib().moe_lora_forward(ctypes.byref(a), _stream()), "moe_lora_forward")
+    else:
+        if len(events) != 2 * len(FORWARD_STAGES):
+            raise ValueError("events needs one pair per forward stage")
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().moe_lora_forward_events(ctypes.byref(a), _stream(), arr),
+               "moe_lora_forward_events")
+    return y
+
+
+def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True) -> torch.Tensor:
+    """info -> align -> forward on a dict from ``workloads.generate``."""
+    T = inputs["x"].shape[0]
+    k = inputs["topk_ids"].shape[1]
+    E = inputs["w_gate_up"].shape[0]
+    L = inputs["lora_ranks"].numel() if with_lora and "a_gate" in inputs else 0
+    ranks = inputs["lora_ranks"]
+    en, mp = moe_lora_info(T, inputs["seg_indptr"], ranks, inputs["weight_indices"],
+                           max_len=inputs["meta"]["max_seg_len"])
+    al = moe_lora_align(inputs["topk_ids"], mp, en if L > 0 else None, E, L, block_m)
+    pools = {n: inputs[n] for n in _POOLS} if L > 0 else None
+    return moe_lora_forward(inputs["x"], inputs["topk_weights"], inputs["w_gate_up"],
+                            inputs["w_down"], al, k, ranks if L > 0 else None,
+                            inputs["scaling"] if L > 0 else None, pools)

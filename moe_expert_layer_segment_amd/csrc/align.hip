@@ -1,0 +1,251 @@
+// Bucketing of (token, expert) pairs by (expert, adapter) -- the align step of
+// the MoE-LoRA layer (SGLang PR #14105 page, section 实现拆解: tokens are sorted
+// by LoRA adapter and expert id before the grouped GEMMs).
+//
+// A stable counting sort over keys e * (L + 1) + (a_eff + 1) in three launches:
+//   1. count   -- each workgroup takes a chunk of pairs; each of its waves ranks
+//                 its pairs among equal keys with a bitwise ballot match (one
+//                 ballot per key bit, no loop over distinct keys) and an LDS
+//                 histogram, so the rank is the pair's order inside the chunk.
+//   2. scan    -- one workgroup: per key, prefix over chunks; bucket sizes padded
+//                 to block_m; exclusive scan over keys; tile counts per expert.
+//   3. scatter -- one thread per output row and per pair: pairs go to
+//                 bucket offset + chunk prefix + rank; pads, tile tables and the
+//                 unused tail are filled by binary search over bucket starts.
+// Every output word up to the capacity is written.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moelora {
+
+static constexpr int kAlignSteps = 8;       // 64-pair steps per wave in the count kernel
+static constexpr int kScanThreads = 1024;
+static constexpr int kScatterThreads = 256;
+
+int align_waves_for_keys(int64_t K) {
+  if (K <= 8192) return 4;
+  if (K <= 16384) return 2;
+  return 1;
+}
+
+int64_t align_chunk_pairs(int64_t K) { return (int64_t)align_waves_for_keys(K) * kAlignSteps * 64; }
+
+AlignWs align_ws_layout(int64_t P, int64_t K) {
+  AlignWs w;
+  int64_t ch = align_chunk_pairs(K);
+  w.nchunks = P > 0 ? ceil_div(P, ch) : 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
+  w.rank_off = take(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+  w.cnt_off = take(sizeof(int32_t) * (size_t)(w.nchunks * K));
+  w.bstart_off = take(sizeof(int32_t) * (size_t)(K + 1));
+  w.btotal_off = take(sizeof(int32_t) * (size_t)K);
+  w.bytes = off;
+  return w;
+}
+
+// key of pair p, or -1 when its expert id is out of range
+__device__ inline int pair_key(int p, int k, int E, int L, const int32_t* __restrict__ topk_ids,
+                               const int32_t* __restrict__ mapping,
+                               const int32_t* __restrict__ enabled) {
+  int e = topk_ids[p];
+  if (e < 0 || e >= E) return -1;
+  int a = mapping[p / k];
+  int a_eff = (a >= 0 && a < L && enabled[a] == 1) ? a : -1;
+  return e * (L + 1) + (a_eff + 1);
+}
+
+__global__ void __launch_bounds__(256)
+align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves,
+                   const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ mapping,
+                   const int32_t* __restrict__ enabled, int32_t* __restrict__ ws_rank,
+                   int32_t* __restrict__ ws_cnt) {
+  extern __shared__ uint16_t hist[];  // [waves][K]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint16_t* h = hist + (size_t)wave * K;
+  for (int i = lane; i < K; i += 64) h[i] = 0;
+
+  const int chunk = blockIdx.x;
+  const int64_t chunk_pairs = (int64_t)waves * kAlignSteps * 64;
+  const int64_t wbase = chunk * chunk_pairs + (int64_t)wave * kAlignSteps * 64;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+
+  int keys[kAlignSteps], ranks[kAlignSteps];
+#pragma unroll
+  for (int s = 0; s < kAlignSteps; ++s) {
+    const int64_t p = wbase + s * 64 + lane;
+    int key = -1;
+    if (p < P) key = pair_key((int)p, k, E, L, topk_ids, mapping, enabled);
+    const bool valid = key >= 0;
+    // lanes holding the same key: AND of per-bit ballots
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < key_bits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    int r = 0;
+    if (valid) {
+      const int before = __popcll(m & lt_mask);
+      const int old = h[key];
+      r = old + before;
+      if (before == 0) h[key] = (uint16_t)(old + __popcll(m));
+    }
+    keys[s] = key;
+    ranks[s] = r;
+  }
+  __syncthreads();
+  // exclusive prefix over waves for each key; chunk totals to global
+  for (int key = threadIdx.x; key < K; key += blockDim.x) {
+    int sum = 0;
+    for (int w = 0; w < waves; ++w) {
+      int c = hist[(size_t)w * K + key];
+      hist[(size_t)w * K + key] = (uint16_t)sum;
+      sum += c;
+    }
+    ws_cnt[(int64_t)chunk * K + key] = sum;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kAlignSteps; ++s) {
+    const int64_t p = wbase + s * 64 + lane;
+    if (p < P && keys[s] >= 0) ws_rank[p] = ranks[s] + h[keys[s]];
+  }
+}
+
+// exclusive scan of one int per thread over a kScanThreads workgroup
+__device__ inline int block_exclusive_scan(int v, int* lds_waves, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      int c = lds_waves[w];
+      lds_waves[w] = run;
+      run += c;
+    }
+    lds_waves[kScanThreads / 64] = run;
+  }
+  __syncthreads();
+  int res = lds_waves[wave] + x - v;
+  *total = lds_waves[kScanThreads / 64];
+  __syncthreads();
+  return res;
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+align_scan_kernel(int nchunks, int K, int E, int L, int BM, int32_t* __restrict__ ws_cnt,
+                  int32_t* __restrict__ ws_bstart, int32_t* __restrict__ ws_btotal,
+                  int32_t* __restrict__ expert_tile_offsets, int32_t* __restrict__ num_rows_padded) {
+  __shared__ int lds_waves[kScanThreads / 64 + 1];
+  const int kpt = (K + kScanThreads - 1) / kScanThreads;
+  const int k0 = min(K, (int)threadIdx.x * kpt), k1 = min(K, k0 + kpt);
+  int mine = 0;
+  for (int key = k0; key < k1; ++key) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int64_t idx = (int64_t)c * K + key;
+      int v = ws_cnt[idx];
+      ws_cnt[idx] = run;
+      run += v;
+    }
+    ws_btotal[key] = run;
+    mine += (int)round_up(run, BM);
+  }
+  int total = 0;
+  int start = block_exclusive_scan(mine, lds_waves, &total);
+  for (int key = k0; key < k1; ++key) {
+    ws_bstart[key] = start;
+    for (int c = 0; c < nchunks; ++c) ws_cnt[(int64_t)c * K + key] += start;
+    start += (int)round_up(ws_btotal[key], BM);
+  }
+  if (threadIdx.x == 0) {
+    ws_bstart[K] = total;
+    num_rows_padded[0] = total;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += kScanThreads)
+    expert_tile_offsets[e] = (e < E ? ws_bstart[e * (L + 1)] : total) / BM;
+}
+
+__global__ void __launch_bounds__(kScatterThreads)
+align_scatter_kernel(int P, int k, int E, int L, int K, int BM, int64_t cap, int64_t chunk_pairs,
+                     const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ mapping,
+                     const int32_t* __restrict__ enabled, const int32_t* __restrict__ ws_rank,
+                     const int32_t* __restrict__ ws_off, const int32_t* __restrict__ ws_bstart,
+                     const int32_t* __restrict__ ws_btotal, int32_t* __restrict__ sorted_ids,
+                     int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_lora) {
+  const int64_t i = (int64_t)blockIdx.x * kScatterThreads + threadIdx.x;
+  if (i < P) {
+    int key = pair_key((int)i, k, E, L, topk_ids, mapping, enabled);
+    if (key >= 0) {
+      int64_t pos = (int64_t)ws_off[(i / chunk_pairs) * K + key] + ws_rank[i];
+      if (pos >= 0 && pos < cap) sorted_ids[pos] = (int32_t)i;
+    }
+  }
+  if (i < cap) {
+    const int rows = ws_bstart[K];
+    if (i >= rows) {
+      sorted_ids[i] = P;
+      if (i % BM == 0) {
+        tile_expert[i / BM] = -1;
+        tile_lora[i / BM] = -1;
+      }
+    } else {
+      int lo = 0, hi = K;  // largest key with bstart[key] <= i
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (ws_bstart[mid] <= i) lo = mid; else hi = mid;
+      }
+      if (i - ws_bstart[lo] >= ws_btotal[lo]) sorted_ids[i] = P;
+      if (i % BM == 0) {
+        tile_expert[i / BM] = lo / (L + 1);
+        tile_lora[i / BM] = lo % (L + 1) - 1;
+      }
+    }
+  }
+}
+
+hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
+                        const int32_t* topk_ids, const int32_t* mapping, const int32_t* enabled,
+                        int32_t* sorted_ids, int32_t* tile_expert, int32_t* tile_lora,
+                        int32_t* expert_tile_offsets, int32_t* num_rows_padded, void* workspace,
+                        hipStream_t stream) {
+  const int64_t P = (int64_t)T * k;
+  const int64_t K = (int64_t)E * (L + 1);
+  const AlignWs w = align_ws_layout(P, K);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ws_rank = reinterpret_cast<int32_t*>(ws + w.rank_off);
+  int32_t* ws_cnt = reinterpret_cast<int32_t*>(ws + w.cnt_off);
+  int32_t* ws_bstart = reinterpret_cast<int32_t*>(ws + w.bstart_off);
+  int32_t* ws_btotal = reinterpret_cast<int32_t*>(ws + w.btotal_off);
+  const int waves = align_waves_for_keys(K);
+  int key_bits = 0;
+  while ((int64_t(1) << key_bits) < K) ++key_bits;
+  const size_t lds = (size_t)waves * K * sizeof(uint16_t);
+
+  hipLaunchKernelGGL(align_count_kernel, dim3((unsigned)w.nchunks), dim3(64 * waves), lds, stream,
+                     (int)P, k, E, L, (int)K, key_bits, waves, topk_ids, mapping, enabled, ws_rank,
+                     ws_cnt);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, (int)w.nchunks,
+                     (int)K, E, L, BM, ws_cnt, ws_bstart, ws_btotal, expert_tile_offsets,
+                     num_rows_padded);
+  const int64_t cap = align_capacity(P, E, L, BM);
+  const int64_t n = cap > P ? cap : P;
+  if (n > 0) {
+    hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ceil_div(n, kScatterThreads)),
+                       dim3(kScatterThreads), 0, stream, (int)P, k, E, L, (int)K, BM, cap,
+                       align_chunk_pairs(K), topk_ids, mapping, enabled, ws_rank, ws_cnt,
+                       ws_bstart, ws_btotal, sorted_ids, tile_expert, tile_lora);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moelora

@@ -1,0 +1,76 @@
+// Shared device helpers of the gfx950 MoE-LoRA kernels: element types, MFMA
+// fragment operations and small integer utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Element traits.  A "frag" is the 8 consecutive K elements one lane feeds to a
+// 16x16 MFMA block per 32-deep K step: one v_mfma_f32_16x16x32_bf16 for bf16,
+// eight v_mfma_f32_16x16x4_f32 for fp32 (the K order inside a 32-step is
+// permuted identically for both operands, which leaves the dot product intact).
+template <typename T> struct Elt;
+
+template <> struct Elt<bf16_t> {
+  typedef bf16x8 frag;
+  static constexpr int kChunk = 8;  // elements per 16-byte chunk
+  __device__ static inline floatx4 mma(const frag& a, const frag& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline bf16_t from_float(float v) { return (bf16_t)v; }
+  __device__ static inline float to_float(bf16_t v) { return (float)v; }
+  __device__ static inline frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16_t)0.0f;
+    return z;
+  }
+};
+
+template <> struct Elt<float> {
+  typedef floatx8 frag;
+  static constexpr int kChunk = 4;
+  __device__ static inline floatx4 mma(const frag& a, const frag& b, floatx4 c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static inline float from_float(float v) { return v; }
+  __device__ static inline float to_float(float v) { return v; }
+  __device__ static inline frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = 0.0f;
+    return z;
+  }
+};
+
+// Load one frag (8 consecutive elements, 16 B for bf16 / 32 B for fp32) from
+// global memory.
+template <typename T>
+__device__ inline typename Elt<T>::frag load_frag_global(const T* p) {
+  return *reinterpret_cast<const typename Elt<T>::frag*>(p);
+}
+
+// SiLU(v) = v * sigmoid(v) = v / (1 + e^-v), with e^-v evaluated as
+// 2^(-v * log2(e)) on the hardware exp2 unit.
+__device__ inline float silu_f(float v) {
+  const float kLog2e = 1.4426950408889634f;
+  float e = __builtin_amdgcn_exp2f(-v * kLog2e);
+  return v / (1.0f + e);
+}
+
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace moelora

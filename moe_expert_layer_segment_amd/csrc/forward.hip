@@ -1,0 +1,646 @@
+// The MoE-LoRA layer forward on gfx950 (SGLang PR #14105 page, "LoRA on MoE
+// expert layers", section 实现拆解: y = (W_down + s B_d A_d)[SiLU((W_gate + s B_g A_g)x)
+// * ((W_up + s B_u A_u)x)], summed over the top-k experts with the router weights).
+//
+// Launch sequence on one stream, no host synchronisation:
+//   plan     -- one workgroup turns expert_tile_offsets into GEMM work items
+//               (row ranges of one expert, at most kBM rows each).
+//   shrink_x -- per 16-row group with an adapter: h_gu = s * [x A_g^T | x A_u^T]
+//               (rank columns beyond the slot rank are zero).
+//   gate_up  -- grouped MFMA GEMM over the work items: x rows gathered by pair id
+//               times W_gate / W_up rows; LoRA expand h_g B_g, h_u B_u added to the
+//               accumulators of each 16-row group; SiLU(gate) * up epilogue -> act.
+//   shrink_a -- h_d = s * act A_d^T per 16-row group.
+//   down     -- grouped MFMA GEMM act * W_down^T + h_d B_d, times the router weight,
+//               written to z in pair order (fp32).
+//   combine  -- y[t] = sum_j z[t*k + j] for j = 0..k-1 in order (fp32), cast to dtype.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moelora {
+
+// --------------------------------------------------------------------------
+// plan: GEMM work items
+// --------------------------------------------------------------------------
+static constexpr int kPlanThreads = 1024;
+
+__global__ void __launch_bounds__(kPlanThreads)
+plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert_tile_offsets,
+            int4* __restrict__ items, int32_t* __restrict__ item_count, int max_items) {
+  __shared__ int lds_waves[kPlanThreads / 64 + 1];
+  const int ept = (E + kPlanThreads - 1) / kPlanThreads;
+  const int e0 = min(E, (int)threadIdx.x * ept), e1 = min(E, e0 + ept);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) {
+    int rows = (expert_tile_offsets[e + 1] - expert_tile_offsets[e]) * BM;
+    mine += (rows + rows_per_item - 1) / rows_per_item;
+  }
+  // exclusive scan over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      int c = lds_waves[w];
+      lds_waves[w] = run;
+      run += c;
+    }
+    lds_waves[kPlanThreads / 64] = run;
+  }
+  __syncthreads();
+  int start = lds_waves[wave] + x - mine;
+  for (int e = e0; e < e1; ++e) {
+    int row0 = expert_tile_offsets[e] * BM;
+    int rows = (expert_tile_offsets[e + 1] - expert_tile_offsets[e]) * BM;
+    for (int r = 0; r < rows; r += rows_per_item) {
+      if (start < max_items) items[start] = make_int4(row0 + r, min(rows_per_item, rows - r), e, 0);
+      ++start;
+    }
+  }
+  if (threadIdx.x == 0) item_count[0] = min(lds_waves[kPlanThreads / 64], max_items);
+}
+
+// --------------------------------------------------------------------------
+// shrink: h[row, pool*RP + q] = s_l * sum_k a_src[row, k] * A_pool[l, e, q, k]
+// for q < r_l (zero for r_l <= q < RP).  One wave per 16-row group.
+// --------------------------------------------------------------------------
+template <typename T>
+struct ShrinkArgs {
+  const T* src;               // x [T, K] (gathered) or act [cap, K] (direct)
+  const int32_t* sorted_ids;  // gathered mode: pair id of each row
+  int gathered, top_k, P;
+  int64_t K;                  // contraction length (H or I)
+  const T* pool0;             // [L, E, R, K]
+  const T* pool1;             // second pool or null
+  int R, RP, L, E, BM;
+  const int32_t* tile_expert;
+  const int32_t* tile_lora;
+  const int32_t* num_rows_padded;
+  const int32_t* lora_ranks;
+  const float* scaling;
+  T* h;                       // [cap, npools * RP]
+  int64_t cap;                // rows of h / act / sorted_ids
+};
+
+template <typename T, int NPOOL>
+__global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
+  typedef Elt<T> E_;
+  typedef typename E_::frag frag;
+  constexpr int NQB = 4;  // up to 64 rank columns per pool = 4 blocks of 16
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row0 = g * 16;
+  if (row0 >= a.num_rows_padded[0] || row0 + 16 > a.cap) return;
+  const int tile = (int)(row0 / a.BM);
+  const int l = a.tile_lora[tile];
+  if (l < 0 || l >= a.L) return;
+  const int e = a.tile_expert[tile];
+  if (e < 0 || e >= a.E) return;
+  const int r = min(a.lora_ranks[l], a.R);
+  const float s = a.scaling[l];
+  const int HS = NPOOL * a.RP;
+  T* hrow_base = a.h + row0 * HS;
+  if (r <= 0) {
+    // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
+    for (int i = lane; i < 16 * HS; i += 64) hrow_base[i] = E_::from_float(0.0f);
+    return;
+  }
+  // A operand row of this lane
+  const int my_row = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const T* arow = nullptr;
+  {
+    int64_t row = row0 + my_row;
+    if (a.gathered) {
+      int p = a.sorted_ids[row];
+      if (p < a.P) arow = a.src + (int64_t)(p / a.top_k) * a.K;
+    } else {
+      arow = a.src + row * a.K;
+    }
+  }
+  const T* prow[NPOOL][NQB];
+  const int nqb = (r + 15) / 16;
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi) {
+    const T* pool = pi == 0 ? a.pool0 : a.pool1;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      int q = qb * 16 + my_row;
+      prow[pi][qb] = (q < r) ? pool + (((int64_t)l * a.E + e) * a.R + q) * a.K : nullptr;
+    }
+  }
+  floatx4 acc[NPOOL][NQB];
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) acc[pi][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t k0 = 0; k0 < a.K; k0 += 32) {
+    frag av = arow ? load_frag_global<T>(arow + k0 + kq) : E_::zero();
+#pragma unroll
+    for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (qb < nqb) {
+          frag bv = prow[pi][qb] ? load_frag_global<T>(prow[pi][qb] + k0 + kq) : E_::zero();
+          acc[pi][qb] = E_::mma(av, bv, acc[pi][qb]);
+        }
+      }
+  }
+  // C layout: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 block
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int col = qb * 16 + (lane & 15);
+      if (col >= a.RP) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = (lane >> 4) * 4 + i;
+        float v = (qb < nqb && col < r) ? s * acc[pi][qb][i] : 0.0f;
+        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = E_::from_float(v);
+      }
+    }
+}
+
+// --------------------------------------------------------------------------
+// grouped GEMM with fused LoRA expand
+// --------------------------------------------------------------------------
+template <typename T>
+struct GemmArgs {
+  const int4* items;
+  const int32_t* item_count;
+  int max_items, n_tiles;
+  // A operand
+  const T* a_src;             // x [T, K] (gate_up, gathered) or act [cap, K] (down)
+  const int32_t* sorted_ids;
+  int top_k, P;
+  int64_t K;
+  // B operand: weights [E, NB_rows, K]
+  const T* w;
+  int64_t n_out;              // output columns (I for gate_up, H for down)
+  int64_t w_rows;             // rows per expert of w (2I or H)
+  // LoRA
+  const int32_t* tile_lora;
+  int BM_tile;
+  const int32_t* lora_ranks;
+  const T* h;                 // [cap, HS]
+  int HS, RP, R, L, E;
+  const T* b_pool0;           // [L, E, R, n_out] (gate or down)
+  const T* b_pool1;           // [L, E, R, n_out] (up) or null
+  // outputs
+  T* act;                     // gate_up: [cap, n_out]
+  float* z;                   // down: [P, n_out]
+  const float* topk_weights;
+  int64_t cap;                // rows of sorted_ids / act / h
+};
+
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  // consecutive logical ids on the same XCD (workgroups are dealt round-robin
+  // over the 8 XCDs), so tiles that share a weight block share an L2
+  const int q = nblocks / 8;
+  if (bid >= q * 8) return bid;
+  return (bid % 8) * q + bid / 8;
+}
+
+template <typename T, int BM, int BN, bool GATE_UP>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
+  typedef Elt<T> E_;
+  typedef typename E_::frag frag;
+  constexpr int ROWB = 128;                       // bytes per LDS tile row (BK * sizeof(T))
+  constexpr int BK = ROWB / sizeof(T);            // 64 bf16 / 32 fp32
+  constexpr int CPR = 8;                          // 16-byte chunks per row
+  constexpr int A_CH = BM * CPR / 256;            // chunks per thread
+  constexpr int B_CH = BN * CPR / 256;
+  constexpr int WM = BM / 2, WN = BN / 2;         // wave tile (2x2 waves)
+  constexpr int MB = WM / 16, NB = WN / 16;
+  constexpr int KSUB = BK / 32;                   // 32-deep MFMA steps per K tile
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+
+  const int nblocks = gridDim.x;
+  const int logical = xcd_remap(blockIdx.x, nblocks);
+  const int item_idx = logical % a.max_items;
+  const int ntile = logical / a.max_items;
+  if (item_idx >= a.item_count[0] || ntile >= a.n_tiles) return;
+  const int4 item = a.items[item_idx];
+  const int64_t row0 = item.x;
+  const int nrows = item.y;
+  const int e = item.z;
+  if (row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) || (row0 & 15) || row0 + nrows > a.cap ||
+      e < 0 || e >= a.E)
+    return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // output column base of this workgroup
+  const int64_t n0 = GATE_UP ? (int64_t)ntile * (BN / 2) : (int64_t)ntile * BN;
+
+  // ---- per-thread global source rows --------------------------------------
+  const T* a_ptr[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c / CPR, kc = c % CPR;
+    const T* p = nullptr;
+    if (r < nrows) {
+      if (GATE_UP) {
+        int pid = a.sorted_ids[row0 + r];
+        if (pid < a.P) p = a.a_src + (int64_t)(pid / a.top_k) * a.K;
+      } else {
+        p = a.a_src + (row0 + r) * a.K;
+      }
+    }
+    a_ptr[i] = p ? p + kc * E_::kChunk : nullptr;
+  }
+  const T* b_ptr[B_CH];
+  const T* wexp = a.w + (int64_t)e * a.w_rows * a.K;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + 256 * i;
+    const int n = c / CPR, kc = c % CPR;
+    int64_t wrow;
+    bool ok;
+    if (GATE_UP) {
+      const int64_t col = n0 + (n % (BN / 2));
+      ok = col < a.n_out;
+      wrow = (n < BN / 2) ? col : a.n_out + col;
+    } else {
+      wrow = n0 + n;
+      ok = wrow < a.n_out;
+    }
+    b_ptr[i] = ok ? wexp + wrow * a.K + kc * E_::kChunk : nullptr;
+  }
+
+  int4v a_reg[A_CH], b_reg[B_CH];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      a_reg[i] = a_ptr[i] ? *reinterpret_cast<const int4v*>(a_ptr[i] + k0) : int4v{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i)
+      b_reg[i] = b_ptr[i] ? *reinterpret_cast<const int4v*>(b_ptr[i] + k0) : int4v{0, 0, 0, 0};
+  };
+  auto lstore = [&](int buf) {
+    char* base = lds[buf];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CPR, kc = c % CPR;
+      *reinterpret_cast<int4v*>(base + r * ROWB + ((kc ^ (r & 7)) * 16)) = a_reg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + 256 * i;
+      const int n = c / CPR, kc = c % CPR;
+      *reinterpret_cast<int4v*>(base + (BM + n) * ROWB + ((kc ^ (n & 7)) * 16)) = b_reg[i];
+    }
+  };
+  // one frag (8 K elements starting at kel) of LDS row `row`
+  auto lfrag = [&](const char* base, int row, int kel) -> frag {
+    if constexpr (sizeof(T) == 2) {
+      const int kc = kel >> 3;
+      return *reinterpret_cast<const frag*>(base + row * ROWB + ((kc ^ (row & 7)) * 16));
+    } else {
+      const int kc = kel >> 2;
+      floatx4 lo = *reinterpret_cast<const floatx4*>(base + row * ROWB + ((kc ^ (row & 7)) * 16));
+      floatx4 hi = *reinterpret_cast<const floatx4*>(base + row * ROWB + (((kc + 1) ^ (row & 7)) * 16));
+      frag f;
+      f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+      f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+      return f;
+    }
+  };
+  // LDS row of B for wave column block nb
+  auto b_row_of = [&](int nb) -> int {
+    if (GATE_UP) {
+      // first NB/2 blocks: gate columns, last NB/2: the matching up columns
+      const int half = NB / 2;
+      const int cb = (nb < half) ? nb : nb - half;
+      const int n = wn * (WN / 2) + cb * 16 + (lane & 15);
+      return BM + ((nb < half) ? n : BN / 2 + n);
+    } else {
+      return BM + wn * WN + nb * 16 + (lane & 15);
+    }
+  };
+
+  floatx4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nk = a.K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const char* base = lds[buf];
+#pragma unroll
+    for (int ks = 0; ks < KSUB; ++ks) {
+      const int kel = ks * 32 + (lane >> 4) * 8;
+      frag af[MB], bfr[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[i] = lfrag(base, wm * WM + i * 16 + (lane & 15), kel);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bfr[j] = lfrag(base, b_row_of(j), kel);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = E_::mma(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] per 16-row group
+  if (a.h != nullptr) {
+    int cached_l = -1;
+    frag bl[NB][2];   // up to RP = 64 -> two 32-deep steps
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int rloc = wm * WM + i * 16;
+      if (rloc >= nrows) continue;
+      const int64_t grow = row0 + rloc;
+      const int l = a.tile_lora[grow / a.BM_tile];
+      if (l < 0 || l >= a.L) continue;
+      const int r = min(a.lora_ranks[l], a.R);
+      if (r <= 0) continue;
+      const int nqs = (r + 31) / 32;
+      if (l != cached_l) {
+        cached_l = l;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const T* pool = a.b_pool0;
+          int cb = j;
+          if (GATE_UP && j >= NB / 2) { pool = a.b_pool1; cb = j - NB / 2; }
+          const int64_t col = n0 + (GATE_UP ? wn * (WN / 2) : wn * WN) + cb * 16 + (lane & 15);
+          const T* pbase = pool + (((int64_t)l * a.E + e) * a.R) * a.n_out + col;
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) {
+            frag f = E_::zero();
+            if (qs < nqs && col < a.n_out) {
+#pragma unroll
+              for (int v = 0; v < 8; ++v) {
+                const int q = qs * 32 + (lane >> 4) * 8 + v;
+                if (q < r) f[v] = pbase[(int64_t)q * a.n_out];
+              }
+            }
+            bl[j][qs] = f;
+          }
+        }
+      }
+      const T* hrow = a.h + (grow + (lane & 15)) * a.HS;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (qs >= nqs) continue;
+        const int q0 = qs * 32 + (lane >> 4) * 8;
+        frag h0 = load_frag_global<T>(hrow + q0);
+        frag h1 = GATE_UP ? load_frag_global<T>(hrow + a.RP + q0) : h0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const bool up = GATE_UP && j >= NB / 2;
+          acc[i][j] = E_::mma(up ? h1 : h0, bl[j][qs], acc[i][j]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  if (GATE_UP) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int j = 0; j < NB / 2; ++j) {
+        const int64_t col = n0 + wn * (WN / 2) + j * 16 + (lane & 15);
+        if (col >= a.n_out) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rloc = wm * WM + i * 16 + (lane >> 4) * 4 + v;
+          if (rloc >= nrows) continue;
+          const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
+          a.act[(row0 + rloc) * a.n_out + col] = E_::from_float(silu_f(g) * u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rloc = wm * WM + i * 16 + (lane >> 4) * 4 + v;
+        if (rloc >= nrows) continue;
+        const int pid = a.sorted_ids[row0 + rloc];
+        if (pid >= a.P) continue;
+        const float wgt = a.topk_weights[pid];
+        float* zrow = a.z + (int64_t)pid * a.n_out;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
+          if (col < a.n_out) zrow[col] = wgt * acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// combine: y[t, c] = sum_j z[t*k + j, c]  (j in order, fp32)
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ z, T* __restrict__ y, int64_t T_, int k, int64_t H) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= T_ * H) return;
+  const int64_t t = i / H, c = i % H;
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    floatx4 v = *reinterpret_cast<const floatx4*>(z + (t * k + j) * H + c);
+    s += v;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[i + q] = Elt<T>::from_float(s[q]);
+}
+
+// --------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------
+template <typename T> struct TileCfg;
+template <> struct TileCfg<bf16_t> { static constexpr int BM = 128, BN = 128; };
+template <> struct TileCfg<float> { static constexpr int BM = 64, BN = 64; };
+
+static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : TileCfg<float>::BM; }
+
+ForwardWs forward_ws_layout(const ForwardProblem& p) {
+  ForwardWs w;
+  const int64_t P = p.T * p.k;
+  const size_t esz = p.dtype == 1 ? 2 : 4;
+  w.cap = align_capacity(P, p.E, p.L, p.BM);
+  const int rpi = rows_per_item(p.dtype);
+  w.max_items = ceil_div(w.cap, rpi) + (P < p.E ? P : p.E);
+  if (w.max_items < 1) w.max_items = 1;
+  w.RP = p.L > 0 ? round_up(p.R > 0 ? p.R : 1, 32) : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
+  w.items_off = take(sizeof(int4) * (size_t)w.max_items);
+  w.count_off = take(sizeof(int32_t) * 4);
+  w.hgu_off = take(p.L > 0 ? esz * (size_t)w.cap * 2 * w.RP : 0);
+  w.act_off = take(esz * (size_t)w.cap * p.I);
+  w.hd_off = take(p.L > 0 ? esz * (size_t)w.cap * w.RP : 0);
+  w.z_off = take(sizeof(float) * (size_t)P * p.H);
+  w.bytes = off;
+  return w;
+}
+
+template <typename T>
+static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
+                             hipEvent_t* events) {
+  // optional measurement: events[2s] / events[2s+1] bracket stage s
+  auto mark = [&](int idx) {
+    if (events && events[idx]) (void)hipEventRecord(events[idx], stream);
+  };
+  const ForwardWs w = forward_ws_layout(p);
+  char* ws = static_cast<char*>(workspace);
+  int4* items = reinterpret_cast<int4*>(ws + w.items_off);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + w.count_off);
+  T* hgu = reinterpret_cast<T*>(ws + w.hgu_off);
+  T* act = reinterpret_cast<T*>(ws + w.act_off);
+  T* hd = reinterpret_cast<T*>(ws + w.hd_off);
+  float* z = reinterpret_cast<float*>(ws + w.z_off);
+  const int64_t P = p.T * p.k;
+  const bool lora = p.L > 0;
+  constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN;
+
+  mark(2 * kStagePlan);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, (int)p.E, (int)p.BM, BM,
+                     p.expert_tile_offsets, items, count, (int)w.max_items);
+  mark(2 * kStagePlan + 1);
+
+  const int64_t groups = w.cap / 16;
+  mark(2 * kStageShrinkX);
+  if (lora && groups > 0) {
+    ShrinkArgs<T> s{};
+    s.src = static_cast<const T*>(p.x);
+    s.sorted_ids = p.sorted_ids;
+    s.gathered = 1;
+    s.top_k = (int)p.k;
+    s.P = (int)P;
+    s.K = p.H;
+    s.pool0 = static_cast<const T*>(p.a_gate);
+    s.pool1 = static_cast<const T*>(p.a_up);
+    s.R = (int)p.R; s.RP = (int)w.RP; s.L = (int)p.L; s.E = (int)p.E; s.BM = (int)p.BM;
+    s.tile_expert = p.tile_expert;
+    s.tile_lora = p.tile_lora;
+    s.num_rows_padded = p.num_rows_padded;
+    s.lora_ranks = p.lora_ranks;
+    s.scaling = p.scaling;
+    s.h = hgu;
+    s.cap = w.cap;
+    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)ceil_div(groups, 4)), dim3(256), 0,
+                       stream, s);
+  }
+  mark(2 * kStageShrinkX + 1);
+
+  GemmArgs<T> g{};
+  g.items = items;
+  g.item_count = count;
+  g.max_items = (int)w.max_items;
+  g.top_k = (int)p.k;
+  g.P = (int)P;
+  g.sorted_ids = p.sorted_ids;
+  g.tile_lora = p.tile_lora;
+  g.BM_tile = (int)p.BM;
+  g.lora_ranks = p.lora_ranks;
+  g.RP = (int)w.RP; g.R = (int)p.R; g.L = (int)p.L; g.E = (int)p.E;
+  g.topk_weights = p.topk_weights;
+  g.cap = w.cap;
+
+  // gate_up
+  {
+    GemmArgs<T> a = g;
+    a.a_src = static_cast<const T*>(p.x);
+    a.K = p.H;
+    a.w = static_cast<const T*>(p.w_gate_up);
+    a.n_out = p.I;
+    a.w_rows = 2 * p.I;
+    a.n_tiles = (int)ceil_div(p.I, BN / 2);
+    a.h = lora ? hgu : nullptr;
+    a.HS = 2 * (int)w.RP;
+    a.b_pool0 = static_cast<const T*>(p.b_gate);
+    a.b_pool1 = static_cast<const T*>(p.b_up);
+    a.act = act;
+    int64_t nblk = (int64_t)a.n_tiles * w.max_items;
+    mark(2 * kStageGateUp);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, true>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    mark(2 * kStageGateUp + 1);
+  }
+  mark(2 * kStageShrinkA);
+  if (lora && groups > 0) {
+    ShrinkArgs<T> s{};
+    s.src = act;
+    s.sorted_ids = p.sorted_ids;
+    s.gathered = 0;
+    s.top_k = (int)p.k;
+    s.P = (int)P;
+    s.K = p.I;
+    s.pool0 = static_cast<const T*>(p.a_down);
+    s.pool1 = nullptr;
+    s.R = (int)p.R; s.RP = (int)w.RP; s.L = (int)p.L; s.E = (int)p.E; s.BM = (int)p.BM;
+    s.tile_expert = p.tile_expert;
+    s.tile_lora = p.tile_lora;
+    s.num_rows_padded = p.num_rows_padded;
+    s.lora_ranks = p.lora_ranks;
+    s.scaling = p.scaling;
+    s.h = hd;
+    s.cap = w.cap;
+    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)ceil_div(groups, 4)), dim3(256), 0,
+                       stream, s);
+  }
+  mark(2 * kStageShrinkA + 1);
+  // down
+  {
+    GemmArgs<T> a = g;
+    a.a_src = act;
+    a.K = p.I;
+    a.w = static_cast<const T*>(p.w_down);
+    a.n_out = p.H;
+    a.w_rows = p.H;
+    a.n_tiles = (int)ceil_div(p.H, BN);
+    a.h = lora ? hd : nullptr;
+    a.HS = (int)w.RP;
+    a.b_pool0 = static_cast<const T*>(p.b_down);
+    a.b_pool1 = nullptr;
+    a.z = z;
+    int64_t nblk = (int64_t)a.n_tiles * w.max_items;
+    mark(2 * kStageDown);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, false>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    mark(2 * kStageDown + 1);
+  }
+  mark(2 * kStageCombine);
+  if (P > 0) {
+    const int64_t n4 = p.T * p.H / 4;
+    hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, stream,
+                       z, static_cast<T*>(p.y), p.T, (int)p.k, p.H);
+  }
+  mark(2 * kStageCombine + 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
+                          hipEvent_t* events) {
+  if (p.dtype == 1) return run_forward<bf16_t>(p, workspace, stream, events);
+  return run_forward<float>(p, workspace, stream, events);
+}
+
+}  // namespace moelora

@@ -1,0 +1,63 @@
+// Host-side launchers of the gfx950 MoE-LoRA kernels (internal to the library;
+// the public surface is the C ABI in include/moe_lora.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moelora {
+
+// ---- align -----------------------------------------------------------------
+struct AlignWs {
+  int64_t nchunks;
+  size_t rank_off, cnt_off, bstart_off, btotal_off, bytes;
+};
+AlignWs align_ws_layout(int64_t num_pairs, int64_t num_keys);
+int64_t align_chunk_pairs(int64_t num_keys);
+
+// rows of the align outputs: P + min(P, E*(L+1)) * (BM - 1), rounded up to BM
+inline int64_t align_capacity(int64_t P, int64_t E, int64_t L, int64_t BM) {
+  int64_t K = E * (L + 1);
+  int64_t nb = P < K ? P : K;
+  int64_t rows = P + nb * (BM - 1);
+  return (rows + BM - 1) / BM * BM;
+}
+
+hipError_t launch_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
+                       const int32_t* seg_indptr, const int32_t* weight_indices,
+                       const int32_t* lora_ranks, int32_t* adapter_enabled,
+                       int32_t* token_lora_mapping, hipStream_t stream);
+
+hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
+                        const int32_t* topk_ids, const int32_t* mapping, const int32_t* enabled,
+                        int32_t* sorted_ids, int32_t* tile_expert, int32_t* tile_lora,
+                        int32_t* expert_tile_offsets, int32_t* num_rows_padded, void* workspace,
+                        hipStream_t stream);
+
+// ---- forward ---------------------------------------------------------------
+struct ForwardProblem {
+  int dtype;  // 0 = fp32, 1 = bf16
+  int64_t T, H, I, E, k, L, R, BM;
+  const void* x;
+  const float* topk_weights;
+  const void *w_gate_up, *w_down;
+  const void *a_gate, *a_up, *b_gate, *b_up, *a_down, *b_down;
+  const int32_t* lora_ranks;
+  const float* scaling;
+  const int32_t *sorted_ids, *tile_expert, *tile_lora, *expert_tile_offsets, *num_rows_padded;
+  void* y;
+};
+
+struct ForwardWs {
+  int64_t cap, max_items, RP;
+  size_t items_off, count_off, hgu_off, act_off, hd_off, z_off, bytes;
+};
+ForwardWs forward_ws_layout(const ForwardProblem& p);
+// stages of the forward, in launch order (index into the optional event pairs)
+enum { kStagePlan = 0, kStageShrinkX, kStageGateUp, kStageShrinkA, kStageDown, kStageCombine,
+       kNumStages };
+hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
+                          hipEvent_t* events);
+
+}  // namespace moelora

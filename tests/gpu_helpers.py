@@ -1,0 +1,86 @@
+"""Helpers shared by the GPU parity tests: host views of device inputs for the
+oracle, and the parity metrics."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from moe_expert_layer_segment_amd import binding, workloads
+
+POOLS = ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
+
+# the benchmark spec acceptance bars for the layer output
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS = 5e-2
+F32_REL_L2 = 1e-4
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class HostView:
+    """Lazy float64 host copy of a device tensor, one index at a time (the
+    oracle reads only the experts / slots the sampled tokens touch)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+
+    def __getitem__(self, idx):
+        key = idx if isinstance(idx, tuple) else (idx,)
+        key = tuple(int(i) for i in key)
+        return self.t[key].float().cpu().numpy().astype(np.float64)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype in (torch.int32, torch.int64):
+        return t.cpu().numpy()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_forward(inp: dict, tokens=None, with_lora=True):
+    """Oracle y (float64) for the device inputs ``inp`` of workloads.generate."""
+    m = inp["meta"]
+    T = inp["x"].shape[0]
+    en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
+                                  m["max_seg_len"])
+    kw = dict(x=to_np(inp["x"]) if tokens is None else HostView(inp["x"]),
+              topk_ids=m["topk_ids"], topk_weights=m["topk_weights"],
+              w_gate_up=HostView(inp["w_gate_up"]), w_down=HostView(inp["w_down"]),
+              lora_ranks=m["lora_ranks"], scaling=m["scaling"],
+              token_lora_mapping=mp, adapter_enabled=en, tokens=tokens)
+    if with_lora and "a_gate" in inp:
+        for n in POOLS:
+            kw[n] = HostView(inp[n])
+    return oracle.moe_lora_forward(**kw)
+
+
+def metrics(got: np.ndarray, ref: np.ndarray):
+    d = got - ref
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
+    mx = float(np.max(np.abs(d))) if d.size else 0.0
+    return rel, mx
+
+
+def assert_layer_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rel, mx = metrics(got, ref)
+    say(f"  {what}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    if dtype == "f32":
+        assert rel <= F32_REL_L2, (what, rel)
+    else:
+        assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS, (what, rel, mx)
+
+
+def gpu_inputs(spec, canary=True, with_lora=True):
+    return workloads.generate(spec, device="cuda", canary=canary, with_lora=with_lora)
+
+
+def run(inp, block_m=16, with_lora=True):
+    y = binding.run_layer(inp, block_m=block_m, with_lora=with_lora)
+    torch.cuda.synchronize()
+    return y

@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, the ctypes struct mirrors the C struct, and host-side validation
+returns the documented status codes before touching any device memory."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from moe_expert_layer_segment_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_lora.h")
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_lora_[a-z_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("moe_lora_info", "moe_lora_align", "moe_lora_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+def test_forward_args_layout_matches_c(tmp_path):
+    fields = [f[0] for f in binding.ForwardArgs._fields_]
+    prog = tmp_path / "layout.c"
+    body = "\n".join(
+        f'  printf("{n} %zu\\n", offsetof(moe_lora_forward_args, {n}));' for n in fields)
+    prog.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"moe_lora.h\"\n"
+        "int main(void) {\n"
+        '  printf("size %zu\\n", sizeof(moe_lora_forward_args));\n' + body + "\n  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(line.split() for line in out if line.strip())
+    assert int(got["size"]) == ctypes.sizeof(binding.ForwardArgs)
+    for n in fields:
+        assert int(got[n]) == getattr(binding.ForwardArgs, n).offset, n
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    for comp, ext in (("gcc", "c"), ("g++", "cpp")):
+        src = tmp_path / f"inc.{ext}"
+        src.write_text('#include "moe_lora.h"\nint main(void) { return MOE_LORA_OK; }\n')
+        subprocess.run([comp, "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o",
+                        str(tmp_path / f"inc_{ext}.o")], check=True)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_status_strings():
+    lib = binding.lib()
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.moe_lora_status_str(st)
+
+
+def test_info_validation_codes():
+    lib = binding.lib()
+    f = lib.moe_lora_info
+    assert f(-1, 1, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(5, 0, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    # the pages' under-coverage example: one request of 300 tokens, max_len 1
+    assert f(300, 1, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == binding.ERR_UNDERCOVER
+    assert f(4, 1, 1, 0, None, FAKE, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 1, 1, 0, FAKE, FAKE, None, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(0, 0, 0, 0, FAKE, None, None, None, None, None) == binding.OK
+
+
+def test_align_validation_codes():
+    lib = binding.lib()
+    f = lib.moe_lora_align
+    args = [FAKE] * 8
+    assert f(4, 2, 8, 2, 15, *args, FAKE, 1 << 30, None) == binding.ERR_INVALID  # block_m
+    assert f(4, 2, 8, 2, 512, *args, FAKE, 1 << 30, None) == binding.ERR_INVALID
+    assert f(4, 9, 8, 2, 16, *args, FAKE, 1 << 30, None) == binding.ERR_INVALID  # k > E
+    assert f(4, 2, 8, 5000, 16, *args, FAKE, 1 << 30, None) == binding.ERR_UNSUPPORTED
+    assert f(4, 2, 8, 2, 16, *args, FAKE, 1, None) == binding.ERR_WORKSPACE
+    assert f(4, 2, 8, 2, 16, *args, None, 1 << 30, None) == binding.ERR_WORKSPACE
+    assert lib.moe_lora_align_capacity_rows(4, 2, 8, 2, 16) == 16 * ((8 + 8 * 15 + 15) // 16)
+    assert lib.moe_lora_align_capacity_rows(4, 2, 8, 2, 17) == -1
+    assert lib.moe_lora_align_workspace_bytes(4, 2, 8, 2, 16) > 0
+
+
+def _fargs(**over):
+    a = binding.ForwardArgs()
+    a.struct_size = ctypes.sizeof(binding.ForwardArgs)
+    a.dtype = binding.DTYPE_BF16
+    a.num_tokens, a.hidden, a.inter, a.num_experts, a.top_k = 8, 128, 256, 4, 2
+    a.num_loras, a.max_rank, a.block_m = 2, 16, 16
+    for n, _ in binding.ForwardArgs._fields_:
+        if n not in ("struct_size", "dtype", "num_tokens", "hidden", "inter", "num_experts",
+                     "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes"):
+            setattr(a, n, 0x1000)
+    a.workspace_bytes = 1
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_forward_validation_codes():
+    lib = binding.lib()
+    call = lambda **o: lib.moe_lora_forward(ctypes.byref(_fargs(**o)), None)  # noqa: E731
+    assert call(dtype=7) == binding.ERR_UNSUPPORTED
+    assert call(struct_size=8) == binding.ERR_INVALID
+    assert call(hidden=100) == binding.ERR_UNSUPPORTED
+    assert call(max_rank=65) == binding.ERR_UNSUPPORTED
+    assert call(top_k=5) == binding.ERR_INVALID
+    assert call(block_m=24) == binding.ERR_INVALID
+    assert call(x=None) == binding.ERR_INVALID
+    assert call(a_down=None) == binding.ERR_INVALID
+    assert call() == binding.ERR_WORKSPACE           # 1-byte workspace
+    assert call(num_loras=0, a_gate=None) == binding.ERR_WORKSPACE  # plain MoE needs no pools
+    ws = lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
+    assert ws > 0
+    assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(dtype=9))) == 0
+    assert call(num_tokens=0) == binding.OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding.moe_lora_info(3, torch.tensor([0, 3], dtype=torch.int32),
+                              torch.tensor([4], dtype=torch.int32),
+                              torch.tensor([0], dtype=torch.int32))
