@@ -155,7 +155,9 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
  *                exactly once, tiles uniform in (expert, slot), each expert's tiles
  *                contiguous and listed by expert_tile_offsets).
  *   workspace    >= moe_lora_forward_workspace_bytes(args) bytes of device memory.
- *   y            [T, H] out       overwritten.
+ *   y            [T, H] out       overwritten, in out_dtype.
+ *   out_dtype    dtype of y: `dtype` (the default layout) or MOE_LORA_F32 (the fp32
+ *                combine result without the final rounding to bf16).
  * num_loras == 0 (pools NULL) runs the plain MoE layer.  H and I must be
  * multiples of 64, R <= 64, top_k <= num_experts.
  */
@@ -184,6 +186,7 @@ typedef struct moe_lora_forward_args {
   void* workspace;
   size_t workspace_bytes;
   void* y;
+  int32_t out_dtype; /* moe_lora_dtype of y */
 } moe_lora_forward_args;
 
 /* Workspace bytes moe_lora_forward needs for the sizes in `args` (0 if invalid). */

@@ -40,7 +40,7 @@ class ForwardArgs(ctypes.Structure):
         ("tile_lora", ctypes.c_void_p), ("expert_tile_offsets", ctypes.c_void_p),
         ("num_rows_padded", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("y", ctypes.c_void_p),
+        ("y", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
     ]
 
 
@@ -212,7 +212,7 @@ _POOLS = ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
 
 
 def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
-                  top_k, y, workspace) -> ForwardArgs:
+                  top_k, y, workspace, out_dtype=None) -> ForwardArgs:
     T, H = x.shape
     E, twoI, H2 = w_gate_up.shape
     I = twoI // 2
@@ -245,6 +245,13 @@ def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, sca
     a = ForwardArgs()
     a.struct_size = ctypes.sizeof(ForwardArgs)
     a.dtype = dt
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    if out_dt == torch.float32:
+        a.out_dtype = DTYPE_F32
+    elif out_dt == x.dtype:
+        a.out_dtype = dt
+    else:
+        raise TypeError(f"unsupported output dtype {out_dt}")
     a.num_tokens, a.hidden, a.inter, a.num_experts, a.top_k = T, H, I, E, top_k
     a.num_loras, a.max_rank, a.block_m = L, R, int(align_out["block_m"])
     a.x, a.topk_weights = x.data_ptr(), topk_weights.data_ptr()
@@ -258,7 +265,7 @@ def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, sca
         _need(align_out[n], n, torch.int32, dev)
         setattr(a, n, align_out[n].data_ptr())
     if y is not None:
-        _need(y, "y", x.dtype, dev, T * H)
+        _need(y, "y", out_dt, dev, T * H)
         a.y = y.data_ptr()
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
@@ -282,20 +289,21 @@ def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: tor
                      pools: Optional[Dict[str, torch.Tensor]] = None,
                      y: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     events=None) -> torch.Tensor:
+                     events=None, out_dtype=None) -> torch.Tensor:
     """The MoE-LoRA layer: returns y [T, H] (written into ``y`` if given).
 
     ``events``: optional sequence of 2 * len(FORWARD_STAGES) raw hipEvent_t
     handles recorded around each kernel stage (measurement only).
     """
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty(x.shape, dtype=x.dtype if out_dtype is None else out_dtype,
+                        device=x.device)
     if workspace is None:
         n = moe_lora_forward_workspace_bytes(x, topk_weights, w_gate_up, w_down, align_out, top_k,
                                              lora_ranks, scaling, pools)
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
     a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
-                      top_k, y, workspace)
+                      top_k, y, workspace, out_dtype)
     if events is None:
         _check(lib().moe_lora_forward(ctypes.byref(a), _stream()), "moe_lora_forward")
     else:
@@ -307,7 +315,8 @@ def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: tor
     return y
 
 
-def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True) -> torch.Tensor:
+def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True,
+              out_dtype=None) -> torch.Tensor:
     """info -> align -> forward on a dict from ``workloads.generate``."""
     T = inputs["x"].shape[0]
     k = inputs["topk_ids"].shape[1]
@@ -320,4 +329,4 @@ def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True) -> torch.
     pools = {n: inputs[n] for n in _POOLS} if L > 0 else None
     return moe_lora_forward(inputs["x"], inputs["topk_weights"], inputs["w_gate_up"],
                             inputs["w_down"], al, k, ranks if L > 0 else None,
-                            inputs["scaling"] if L > 0 else None, pools)
+                            inputs["scaling"] if L > 0 else None, pools, out_dtype=out_dtype)

@@ -86,7 +86,7 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
                                  static_cast<hipStream_t>(stream)));
 }
 
-static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p) {
+static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool check_ptrs) {
   if (!a || a->struct_size < sizeof(moe_lora_forward_args)) return MOE_LORA_ERR_INVALID;
   if (a->dtype != MOE_LORA_F32 && a->dtype != MOE_LORA_BF16) return MOE_LORA_ERR_UNSUPPORTED;
   if (a->num_tokens < 0 || a->hidden <= 0 || a->inter <= 0 || a->num_experts <= 0 ||
@@ -97,7 +97,7 @@ static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p) {
   if (a->max_rank > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
   if ((int64_t)a->num_tokens * a->top_k > INT32_MAX / 2) return MOE_LORA_ERR_UNSUPPORTED;
   if (a->num_loras > 0 && a->max_rank <= 0) return MOE_LORA_ERR_INVALID;
-  if (a->num_tokens > 0) {
+  if (check_ptrs && a->num_tokens > 0) {
     if (!a->x || !a->topk_weights || !a->w_gate_up || !a->w_down || !a->sorted_pair_ids ||
         !a->tile_expert || !a->tile_lora || !a->expert_tile_offsets || !a->num_rows_padded || !a->y)
       return MOE_LORA_ERR_INVALID;
@@ -116,18 +116,20 @@ static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p) {
   p->sorted_ids = a->sorted_pair_ids; p->tile_expert = a->tile_expert; p->tile_lora = a->tile_lora;
   p->expert_tile_offsets = a->expert_tile_offsets; p->num_rows_padded = a->num_rows_padded;
   p->y = a->y;
+  if (a->out_dtype != a->dtype && a->out_dtype != MOE_LORA_F32) return MOE_LORA_ERR_UNSUPPORTED;
+  p->out_f32 = (a->out_dtype == MOE_LORA_F32) && a->dtype != MOE_LORA_F32;
   return MOE_LORA_OK;
 }
 
 size_t moe_lora_forward_workspace_bytes(const moe_lora_forward_args* args) {
   ForwardProblem p;
-  if (to_problem(args, &p) != MOE_LORA_OK) return 0;
+  if (to_problem(args, &p, false) != MOE_LORA_OK) return 0;
   return forward_ws_layout(p).bytes;
 }
 
 static int forward_impl(const moe_lora_forward_args* args, void* stream, void* const* events) {
   ForwardProblem p;
-  int st = to_problem(args, &p);
+  int st = to_problem(args, &p, true);
   if (st != MOE_LORA_OK) return st;
   if (p.T == 0) return MOE_LORA_OK;
   const size_t need = forward_ws_layout(p).bytes;

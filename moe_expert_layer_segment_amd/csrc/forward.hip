@@ -85,7 +85,7 @@ struct ShrinkArgs {
   const int32_t* num_rows_padded;
   const int32_t* lora_ranks;
   const float* scaling;
-  T* h;                       // [cap, npools * RP]
+  float* h;                   // [cap, npools * RP], fp32
   int64_t cap;                // rows of h / act / sorted_ids
 };
 
@@ -106,10 +106,10 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
   const int r = min(a.lora_ranks[l], a.R);
   const float s = a.scaling[l];
   const int HS = NPOOL * a.RP;
-  T* hrow_base = a.h + row0 * HS;
+  float* hrow_base = a.h + row0 * HS;
   if (r <= 0) {
     // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
-    for (int i = lane; i < 16 * HS; i += 64) hrow_base[i] = E_::from_float(0.0f);
+    for (int i = lane; i < 16 * HS; i += 64) hrow_base[i] = 0.0f;
     return;
   }
   // A operand row of this lane
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = (lane >> 4) * 4 + i;
         float v = (qb < nqb && col < r) ? s * acc[pi][qb][i] : 0.0f;
-        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = E_::from_float(v);
+        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
       }
     }
 }
@@ -191,7 +191,7 @@ struct GemmArgs {
   const int32_t* tile_lora;
   int BM_tile;
   const int32_t* lora_ranks;
-  const T* h;                 // [cap, HS]
+  const float* h;             // [cap, HS], fp32 (scaled shrink result)
   int HS, RP, R, L, E;
   const T* b_pool0;           // [L, E, R, n_out] (gate or down)
   const T* b_pool1;           // [L, E, R, n_out] (up) or null
@@ -401,17 +401,35 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
           }
         }
       }
-      const T* hrow = a.h + (grow + (lane & 15)) * a.HS;
+      const float* hrow = a.h + (grow + (lane & 15)) * a.HS;
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         if (qs >= nqs) continue;
         const int q0 = qs * 32 + (lane >> 4) * 8;
-        frag h0 = load_frag_global<T>(hrow + q0);
-        frag h1 = GATE_UP ? load_frag_global<T>(hrow + a.RP + q0) : h0;
+        const floatx8 hg = *reinterpret_cast<const floatx8*>(hrow + q0);
+        const floatx8 hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
+        if constexpr (sizeof(T) == 2) {
+          // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
+          frag g_hi, g_lo, u_hi, u_lo;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const bool up = GATE_UP && j >= NB / 2;
-          acc[i][j] = E_::mma(up ? h1 : h0, bl[j][qs], acc[i][j]);
+          for (int v = 0; v < 8; ++v) {
+            g_hi[v] = (bf16_t)hg[v];
+            g_lo[v] = (bf16_t)(hg[v] - (float)g_hi[v]);
+            u_hi[v] = (bf16_t)hu[v];
+            u_lo[v] = (bf16_t)(hu[v] - (float)u_hi[v]);
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const bool up = GATE_UP && j >= NB / 2;
+            acc[i][j] = E_::mma(up ? u_hi : g_hi, bl[j][qs], acc[i][j]);
+            acc[i][j] = E_::mma(up ? u_lo : g_lo, bl[j][qs], acc[i][j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const bool up = GATE_UP && j >= NB / 2;
+            acc[i][j] = E_::mma(up ? hu : hg, bl[j][qs], acc[i][j]);
+          }
         }
       }
     }
@@ -458,9 +476,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
 // --------------------------------------------------------------------------
 // combine: y[t, c] = sum_j z[t*k + j, c]  (j in order, fp32)
 // --------------------------------------------------------------------------
-template <typename T>
+template <typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ z, T* __restrict__ y, int64_t T_, int k, int64_t H) {
+combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T_ * H) return;
   const int64_t t = i / H, c = i % H;
@@ -470,7 +488,7 @@ combine_kernel(const float* __restrict__ z, T* __restrict__ y, int64_t T_, int k
     s += v;
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) y[i + q] = Elt<T>::from_float(s[q]);
+  for (int q = 0; q < 4; ++q) y[i + q] = Elt<OutT>::from_float(s[q]);
 }
 
 // --------------------------------------------------------------------------
@@ -495,9 +513,9 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
   w.count_off = take(sizeof(int32_t) * 4);
-  w.hgu_off = take(p.L > 0 ? esz * (size_t)w.cap * 2 * w.RP : 0);
+  w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
-  w.hd_off = take(p.L > 0 ? esz * (size_t)w.cap * w.RP : 0);
+  w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * w.RP : 0);
   w.z_off = take(sizeof(float) * (size_t)P * p.H);
   w.bytes = off;
   return w;
@@ -514,9 +532,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   char* ws = static_cast<char*>(workspace);
   int4* items = reinterpret_cast<int4*>(ws + w.items_off);
   int32_t* count = reinterpret_cast<int32_t*>(ws + w.count_off);
-  T* hgu = reinterpret_cast<T*>(ws + w.hgu_off);
+  float* hgu = reinterpret_cast<float*>(ws + w.hgu_off);
   T* act = reinterpret_cast<T*>(ws + w.act_off);
-  T* hd = reinterpret_cast<T*>(ws + w.hd_off);
+  float* hd = reinterpret_cast<float*>(ws + w.hd_off);
   float* z = reinterpret_cast<float*>(ws + w.z_off);
   const int64_t P = p.T * p.k;
   const bool lora = p.L > 0;
@@ -630,8 +648,12 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   mark(2 * kStageCombine);
   if (P > 0) {
     const int64_t n4 = p.T * p.H / 4;
-    hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, stream,
-                       z, static_cast<T*>(p.y), p.T, (int)p.k, p.H);
+    if (p.out_f32)
+      hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, z, static_cast<float*>(p.y), p.T, (int)p.k, p.H);
+    else
+      hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, z, static_cast<T*>(p.y), p.T, (int)p.k, p.H);
   }
   mark(2 * kStageCombine + 1);
   return hipGetLastError();

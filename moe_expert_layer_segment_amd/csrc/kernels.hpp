@@ -47,6 +47,7 @@ struct ForwardProblem {
   const float* scaling;
   const int32_t *sorted_ids, *tile_expert, *tile_lora, *expert_tile_offsets, *num_rows_padded;
   void* y;
+  int out_f32;  // y in fp32 instead of dtype
 };
 
 struct ForwardWs {

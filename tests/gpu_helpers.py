@@ -80,7 +80,7 @@ def gpu_inputs(spec, canary=True, with_lora=True):
     return workloads.generate(spec, device="cuda", canary=canary, with_lora=with_lora)
 
 
-def run(inp, block_m=16, with_lora=True):
-    y = binding.run_layer(inp, block_m=block_m, with_lora=with_lora)
+def run(inp, block_m=16, with_lora=True, out_dtype=None):
+    y = binding.run_layer(inp, block_m=block_m, with_lora=with_lora, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return y

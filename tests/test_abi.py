@@ -110,9 +110,11 @@ def _fargs(**over):
     a.num_loras, a.max_rank, a.block_m = 2, 16, 16
     for n, _ in binding.ForwardArgs._fields_:
         if n not in ("struct_size", "dtype", "num_tokens", "hidden", "inter", "num_experts",
-                     "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes"):
+                     "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes",
+                     "out_dtype"):
             setattr(a, n, 0x1000)
     a.workspace_bytes = 1
+    a.out_dtype = binding.DTYPE_BF16
     for k, v in over.items():
         setattr(a, k, v)
     return a
@@ -122,6 +124,8 @@ def test_forward_validation_codes():
     lib = binding.lib()
     call = lambda **o: lib.moe_lora_forward(ctypes.byref(_fargs(**o)), None)  # noqa: E731
     assert call(dtype=7) == binding.ERR_UNSUPPORTED
+    assert call(out_dtype=5) == binding.ERR_UNSUPPORTED
+    assert call(out_dtype=binding.DTYPE_F32) == binding.ERR_WORKSPACE  # fp32 output is allowed
     assert call(struct_size=8) == binding.ERR_INVALID
     assert call(hidden=100) == binding.ERR_UNSUPPORTED
     assert call(max_rank=65) == binding.ERR_UNSUPPORTED
@@ -133,6 +137,14 @@ def test_forward_validation_codes():
     assert call(num_loras=0, a_gate=None) == binding.ERR_WORKSPACE  # plain MoE needs no pools
     ws = lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
     assert ws > 0
+    # sizing needs no pointers at all
+    bare = _fargs()
+    for n, _ in binding.ForwardArgs._fields_:
+        if n not in ("struct_size", "dtype", "num_tokens", "hidden", "inter", "num_experts",
+                     "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes",
+                     "out_dtype"):
+            setattr(bare, n, None)
+    assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(bare)) == ws
     assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(dtype=9))) == 0
     assert call(num_tokens=0) == binding.OK
 

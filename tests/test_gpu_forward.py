@@ -3,6 +3,11 @@
 Small shapes are compared element by element on every token; the full-size
 workloads are compared on a sample of tokens the oracle computes one by one,
 in the same launch configuration the benchmark times.
+
+The tolerance is applied to the fp32 combine result (out_dtype=float32): a
+bf16 y carries up to half an ulp of final rounding (0.0625 for |y| >= 16),
+which alone can exceed the 5e-2 max-abs bar.  The bf16 output itself is then
+checked to be exactly the round-to-nearest-even of that fp32 result.
 """
 import numpy as np
 import pytest
@@ -16,7 +21,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _y(inp, **kw):
-    return to_np(run(inp, **kw))
+    """fp32 y; for bf16 inputs also checks the bf16 y is its RNE rounding."""
+    y32 = run(inp, out_dtype=torch.float32, **kw)
+    if inp["x"].dtype == torch.bfloat16:
+        y16 = run(inp, **kw)
+        assert y16.dtype == torch.bfloat16
+        assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 y is not the rounded fp32 y"
+    return to_np(y32)
 
 
 def test_config0_fp32_full():
@@ -73,7 +84,8 @@ def test_reductions_to_base():
     inp = gpu_inputs(spec)
     y_base = run(inp, with_lora=False).clone()
     ref_base = oracle_forward(inp, with_lora=False)
-    assert_layer_close(to_np(y_base), ref_base, "bf16", "base")
+    assert_layer_close(to_np(run(inp, with_lora=False, out_dtype=torch.float32)), ref_base,
+                       "bf16", "base")
     # every request without an adapter -> bitwise the base run
     inp_m1 = dict(inp)
     inp_m1["weight_indices"] = torch.full_like(inp["weight_indices"], -1)
@@ -101,7 +113,7 @@ def test_gate_up_adapters_are_distinct():
     for zero in ("b_up", "b_gate"):
         mod = dict(inp)
         mod[zero] = torch.where(torch.isnan(inp[zero]), inp[zero], torch.zeros_like(inp[zero]))
-        got = to_np(run(mod))
+        got = to_np(run(mod, out_dtype=torch.float32))
         ref = oracle_forward(mod)
         assert_layer_close(got, ref, "bf16", f"{zero}=0")
 
