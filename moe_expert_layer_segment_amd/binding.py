@@ -14,7 +14,7 @@ from typing import Dict, Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libmoe_lora.so")
+LIB_PATH = os.environ.get("MOE_LORA_LIB") or os.path.join(_PKG, "lib", "libmoe_lora.so")
 
 OK, ERR_INVALID, ERR_UNDERCOVER, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16 = 0, 1

@@ -91,12 +91,14 @@ struct ShrinkArgs {
 
 template <typename T, int NPOOL>
 __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
+  // one workgroup per 16-row group; its 4 waves take interleaved 32-deep K
+  // steps and their partial sums are added in LDS
   typedef Elt<T> E_;
   typedef typename E_::frag frag;
   constexpr int NQB = 4;  // up to 64 rank columns per pool = 4 blocks of 16
+  __shared__ floatx4 part[3][NPOOL * NQB][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t row0 = g * 16;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
   if (row0 >= a.num_rows_padded[0] || row0 + 16 > a.cap) return;
   const int tile = (int)(row0 / a.BM);
   const int l = a.tile_lora[tile];
@@ -109,7 +111,7 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
   float* hrow_base = a.h + row0 * HS;
   if (r <= 0) {
     // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
-    for (int i = lane; i < 16 * HS; i += 64) hrow_base[i] = 0.0f;
+    for (int i = threadIdx.x; i < 16 * HS; i += 256) hrow_base[i] = 0.0f;
     return;
   }
   // A operand row of this lane
@@ -142,7 +144,8 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) acc[pi][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = 0; k0 < a.K; k0 += 32) {
+#pragma unroll 2
+  for (int64_t k0 = wave * 32; k0 < a.K; k0 += 128) {
     frag av = arow ? load_frag_global<T>(arow + k0 + kq) : E_::zero();
 #pragma unroll
     for (int pi = 0; pi < NPOOL; ++pi)
@@ -154,6 +157,14 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
         }
       }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) part[wave - 1][pi * NQB + qb][lane] = acc[pi][qb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
   // C layout: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 block
 #pragma unroll
   for (int pi = 0; pi < NPOOL; ++pi)
@@ -161,10 +172,13 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
     for (int qb = 0; qb < NQB; ++qb) {
       const int col = qb * 16 + (lane & 15);
       if (col >= a.RP) continue;
+      floatx4 t = acc[pi][qb];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) t += part[w][pi * NQB + qb][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = (lane >> 4) * 4 + i;
-        float v = (qb < nqb && col < r) ? s * acc[pi][qb][i] : 0.0f;
+        float v = (qb < nqb && col < r) ? s * t[i] : 0.0f;
         hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
       }
     }
@@ -173,6 +187,30 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
 // --------------------------------------------------------------------------
 // grouped GEMM with fused LoRA expand
 // --------------------------------------------------------------------------
+// Output-block traits.  bf16 uses v_mfma_f32_32x32x16_bf16 (32x32 blocks; on
+// gfx950 it runs at twice the rate of the 16x16x32 form); fp32 uses eight
+// v_mfma_f32_16x16x4_f32 per 32-deep step on 16x16 blocks.  In both, lane l
+// feeds row / column (l % BS) with the 8 consecutive K elements starting at
+// 8 * (l / BS) of the current KF-deep step.
+template <typename T> struct Blk;
+template <> struct Blk<bf16_t> {
+  static constexpr int BS = 32, KF = 16, ACC = 16;
+  typedef floatx16 acc_t;
+  __device__ static inline acc_t mma(const bf16x8& a, const bf16x8& b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // row (inside the 32x32 block) of accumulator element v of lane `lane`
+  __device__ static inline int row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+};
+template <> struct Blk<float> {
+  static constexpr int BS = 16, KF = 32, ACC = 4;
+  typedef floatx4 acc_t;
+  __device__ static inline acc_t mma(const floatx8& a, const floatx8& b, acc_t c) {
+    return Elt<float>::mma(a, b, c);
+  }
+  __device__ static inline int row(int v, int lane) { return 4 * (lane >> 4) + v; }
+};
+
 template <typename T>
 struct GemmArgs {
   const int4* items;
@@ -183,7 +221,7 @@ struct GemmArgs {
   const int32_t* sorted_ids;
   int top_k, P;
   int64_t K;
-  // B operand: weights [E, NB_rows, K]
+  // B operand: weights [E, w_rows, K]
   const T* w;
   int64_t n_out;              // output columns (I for gate_up, H for down)
   int64_t w_rows;             // rows per expert of w (2I or H)
@@ -202,233 +240,322 @@ struct GemmArgs {
   int64_t cap;                // rows of sorted_ids / act / h
 };
 
+#ifndef MOELORA_GROUP_M
+#define MOELORA_GROUP_M 8
+#endif
+static constexpr int kGroupM = MOELORA_GROUP_M;  // work items per tile-order group
+
 __device__ inline int xcd_remap(int bid, int nblocks) {
-  // consecutive logical ids on the same XCD (workgroups are dealt round-robin
-  // over the 8 XCDs), so tiles that share a weight block share an L2
+  // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of logical tiles so neighbouring tiles share its L2
   const int q = nblocks / 8;
   if (bid >= q * 8) return bid;
   return (bid % 8) * q + bid / 8;
 }
 
-template <typename T, int BM, int BN, bool GATE_UP>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
+// Issue one 16-byte-per-lane global -> LDS load: lane i of the wave writes the
+// 16 bytes at gbase + goff to LDS byte address lds_addr + 16 * i.  The LDS base
+// goes through M0 (saved and restored around the load, so the compiler's view
+// of M0 is unchanged).  The compiler does not track these loads: callers wait
+// for them with an explicit s_waitcnt vmcnt before a barrier.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t lds_addr) {
+  // base and LDS address are wave-uniform: move them to SGPRs explicitly
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint64_t gs = ((uint64_t)ghi << 32) | glo;
+  const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[la]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[go], %[gb]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [la] "s"(la), [go] "v"(goff), [gb] "s"(gs)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  // all of this wave's LDS loads except the newest N have landed, then every
+  // wave of the workgroup has got that far
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GATE_UP>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T> a) {
   typedef Elt<T> E_;
+  typedef Blk<T> B_;
   typedef typename E_::frag frag;
-  constexpr int ROWB = 128;                       // bytes per LDS tile row (BK * sizeof(T))
+  typedef typename B_::acc_t acc_t;
+  constexpr int BS = B_::BS, KF = B_::KF;
+  constexpr int ROWB = 128;                       // bytes per LDS tile row (one K tile)
   constexpr int BK = ROWB / sizeof(T);            // 64 bf16 / 32 fp32
-  constexpr int CPR = 8;                          // 16-byte chunks per row
-  constexpr int A_CH = BM * CPR / 256;            // chunks per thread
-  constexpr int B_CH = BN * CPR / 256;
-  constexpr int WM = BM / 2, WN = BN / 2;         // wave tile (2x2 waves)
-  constexpr int MB = WM / 16, NB = WN / 16;
-  constexpr int KSUB = BK / 32;                   // 32-deep MFMA steps per K tile
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  constexpr int NWAVES = WAVES_M * WAVES_N;
+  constexpr int ROWS = BM + BN;                   // LDS rows per stage: A rows then B rows
+  constexpr int SEGS = ROWS / 8;                  // 1 KB segments (8 rows) per stage
+  constexpr int SEG_PER_WAVE = SEGS / NWAVES;     // DMA instructions per wave per stage
+  constexpr int STAGE_BYTES = ROWS * ROWB;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
+  constexpr int MB = WM / BS, NB = WN / BS;
+  constexpr int KSUB = BK / KF;
+  static_assert(SEGS % NWAVES == 0 && MB >= 1 && NB >= 1, "tile / wave split");
+  static_assert(!GATE_UP || (NB % 2) == 0, "gate/up blocks come in pairs");
+  static_assert(STAGES >= 2, "ring depth");
 
-  __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
 
-  const int nblocks = gridDim.x;
-  const int logical = xcd_remap(blockIdx.x, nblocks);
-  const int item_idx = logical % a.max_items;
-  const int ntile = logical / a.max_items;
-  if (item_idx >= a.item_count[0] || ntile >= a.n_tiles) return;
+  // Persistent tile loop.  Workgroups are dealt round-robin over the 8 XCDs;
+  // each XCD owns a contiguous range of logical tiles and sweeps it in rounds
+  // of (its workgroups) tiles, so the tiles resident on one XCD at a time are
+  // neighbours: kGroupM work items x consecutive column tiles, sharing x rows
+  // and weight columns in that XCD's L2.
+  const int count = min(a.item_count[0], a.max_items);
+  const int total = (int)ceil_div(count, kGroupM) * kGroupM * a.n_tiles;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_round = gridDim.x / 8;
+  const int per_xcd = (total + 7) / 8;
+  const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
+  const int per_group = kGroupM * a.n_tiles;
+  for (int logical = t_begin + slot; logical < t_end; logical += per_round) {
+  const int item_idx = (logical / per_group) * kGroupM + (logical % per_group) % kGroupM;
+  const int ntile = (logical % per_group) / kGroupM;
+  if (item_idx >= count || ntile >= a.n_tiles) continue;
   const int4 item = a.items[item_idx];
   const int64_t row0 = item.x;
   const int nrows = item.y;
   const int e = item.z;
   if (row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) || (row0 & 15) || row0 + nrows > a.cap ||
       e < 0 || e >= a.E)
-    return;
+    continue;
+  __syncthreads();  // the previous tile's last LDS reads are done
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  (void)tid;
+  const int lrow = lane % BS;                     // row / column this lane feeds
+  const int lk = 8 * (lane / BS);                 // K offset of its 8 elements
 
-  // output column base of this workgroup
   const int64_t n0 = GATE_UP ? (int64_t)ntile * (BN / 2) : (int64_t)ntile * BN;
 
-  // ---- per-thread global source rows --------------------------------------
-  const T* a_ptr[A_CH];
+  // ---- DMA source offsets --------------------------------------------------
+  // Stage layout: LDS row r < BM holds A row r, row BM + n holds B row n, 128
+  // bytes (one K tile) each, its eight 16-byte chunks permuted by
+  // slot = chunk ^ swz(row) so fragment reads of 16 / 32 consecutive rows hit
+  // distinct banks.  Wave w fills segments w*SEG_PER_WAVE.. (8 rows each);
+  // lane l of a segment writes row 8*seg + l/8, slot l%8, i.e. global chunk
+  // (l%8) ^ swz(row).  Rows outside the tile (pads, rows past nrows, columns
+  // past n_out) load a valid row instead: MFMA rows / columns are
+  // independent and those results are never stored.
+  auto swz = [](int row) -> int { return (row >> 1) & 7; };
+  const T* a_base = a.a_src;
+  const T* b_base = a.w + (int64_t)e * a.w_rows * a.K;
+  uint32_t src_off[SEG_PER_WAVE];   // byte offsets from a_base / b_base
+  int pidv[SEG_PER_WAVE];
+  if (GATE_UP) {
+    // pair ids of the gathered A rows: clamped, unconditional loads, issued together
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / CPR, kc = c % CPR;
-    const T* p = nullptr;
-    if (r < nrows) {
+    for (int i = 0; i < SEG_PER_WAVE; ++i) {
+      const int row = (wave * SEG_PER_WAVE + i) * 8 + lane / 8;
+      pidv[i] = a.sorted_ids[row0 + min(min(row, BM - 1), nrows - 1)];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SEG_PER_WAVE; ++i) {
+    const int seg = wave * SEG_PER_WAVE + i;
+    const int row = seg * 8 + lane / 8;
+    const int kc = (lane % 8) ^ swz(row);
+    int64_t grow;
+    if (row < BM) {
+      const int r = row;
       if (GATE_UP) {
-        int pid = a.sorted_ids[row0 + r];
-        if (pid < a.P) p = a.a_src + (int64_t)(pid / a.top_k) * a.K;
+        const int pid = r < nrows ? pidv[i] : a.P;
+        grow = pid < a.P ? pid / a.top_k : 0;
       } else {
-        p = a.a_src + (row0 + r) * a.K;
+        grow = row0 + (r < nrows ? r : 0);
+      }
+    } else {
+      const int n = row - BM;
+      if (GATE_UP) {
+        const int64_t col = n0 + (n % (BN / 2));
+        grow = col < a.n_out ? ((n < BN / 2) ? col : a.n_out + col) : 0;
+      } else {
+        grow = n0 + n < a.n_out ? n0 + n : 0;
       }
     }
-    a_ptr[i] = p ? p + kc * E_::kChunk : nullptr;
+    src_off[i] = (uint32_t)((grow * a.K + kc * E_::kChunk) * sizeof(T));
   }
-  const T* b_ptr[B_CH];
-  const T* wexp = a.w + (int64_t)e * a.w_rows * a.K;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  auto issue_stage = [&](int stage_k, int buf) {
+    const uint32_t kbytes = (uint32_t)stage_k * ROWB;
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + 256 * i;
-    const int n = c / CPR, kc = c % CPR;
-    int64_t wrow;
-    bool ok;
-    if (GATE_UP) {
-      const int64_t col = n0 + (n % (BN / 2));
-      ok = col < a.n_out;
-      wrow = (n < BN / 2) ? col : a.n_out + col;
-    } else {
-      wrow = n0 + n;
-      ok = wrow < a.n_out;
-    }
-    b_ptr[i] = ok ? wexp + wrow * a.K + kc * E_::kChunk : nullptr;
-  }
-
-  int4v a_reg[A_CH], b_reg[B_CH];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      a_reg[i] = a_ptr[i] ? *reinterpret_cast<const int4v*>(a_ptr[i] + k0) : int4v{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      b_reg[i] = b_ptr[i] ? *reinterpret_cast<const int4v*>(b_ptr[i] + k0) : int4v{0, 0, 0, 0};
-  };
-  auto lstore = [&](int buf) {
-    char* base = lds[buf];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CPR, kc = c % CPR;
-      *reinterpret_cast<int4v*>(base + r * ROWB + ((kc ^ (r & 7)) * 16)) = a_reg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + 256 * i;
-      const int n = c / CPR, kc = c % CPR;
-      *reinterpret_cast<int4v*>(base + (BM + n) * ROWB + ((kc ^ (n & 7)) * 16)) = b_reg[i];
+    for (int i = 0; i < SEG_PER_WAVE; ++i) {
+      const int seg = wave * SEG_PER_WAVE + i;
+      const void* base = (seg * 8 < BM) ? (const void*)a_base : (const void*)b_base;
+      dma16(base, src_off[i] + kbytes, lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
   };
   // one frag (8 K elements starting at kel) of LDS row `row`
   auto lfrag = [&](const char* base, int row, int kel) -> frag {
     if constexpr (sizeof(T) == 2) {
       const int kc = kel >> 3;
-      return *reinterpret_cast<const frag*>(base + row * ROWB + ((kc ^ (row & 7)) * 16));
+      return *reinterpret_cast<const frag*>(base + row * ROWB + ((kc ^ swz(row)) * 16));
     } else {
       const int kc = kel >> 2;
-      floatx4 lo = *reinterpret_cast<const floatx4*>(base + row * ROWB + ((kc ^ (row & 7)) * 16));
-      floatx4 hi = *reinterpret_cast<const floatx4*>(base + row * ROWB + (((kc + 1) ^ (row & 7)) * 16));
+      floatx4 lo = *reinterpret_cast<const floatx4*>(base + row * ROWB + ((kc ^ swz(row)) * 16));
+      floatx4 hi = *reinterpret_cast<const floatx4*>(base + row * ROWB + (((kc + 1) ^ swz(row)) * 16));
       frag f;
       f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
       f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
       return f;
     }
   };
-  // LDS row of B for wave column block nb
-  auto b_row_of = [&](int nb) -> int {
+  // wave-local column block j -> first output column (act column for gate_up)
+  auto col_of = [&](int j) -> int64_t {
+    if (GATE_UP) return n0 + wn * (WN / 2) + (j % (NB / 2)) * BS;
+    return n0 + wn * WN + j * BS;
+  };
+  // LDS row of B for this lane in column block j
+  auto b_row_of = [&](int j) -> int {
     if (GATE_UP) {
-      // first NB/2 blocks: gate columns, last NB/2: the matching up columns
-      const int half = NB / 2;
-      const int cb = (nb < half) ? nb : nb - half;
-      const int n = wn * (WN / 2) + cb * 16 + (lane & 15);
-      return BM + ((nb < half) ? n : BN / 2 + n);
-    } else {
-      return BM + wn * WN + nb * 16 + (lane & 15);
+      const int n = wn * (WN / 2) + (j % (NB / 2)) * BS + lrow;
+      return BM + ((j < NB / 2) ? n : BN / 2 + n);
     }
+    return BM + wn * WN + j * BS + lrow;
   };
 
-  floatx4 acc[MB][NB];
+  acc_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < B_::ACC; ++v) acc[i][j][v] = 0.0f;
 
-  const int64_t nk = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const char* base = lds[buf];
+  // Fragments are double-buffered in registers: the LDS reads of sub-step
+  // ks+1 are issued before the MFMAs of sub-step ks.
+  frag fa[2][MB], fb[2][NB];
+  auto load_frags = [&](const char* base, int ks, int set) {
+    const int kel = ks * KF + lk;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) fa[set][i] = lfrag(base, wm * WM + i * BS + lrow, kel);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fb[set][j] = lfrag(base, b_row_of(j), kel);
+  };
+  auto mma_frags = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = B_::mma(fa[set][i], fb[set][j], acc[i][j]);
+  };
+  auto compute = [&](int buf) {
+    const char* base = lds + buf * STAGE_BYTES;
+    load_frags(base, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KSUB; ++ks) {
-      const int kel = ks * 32 + (lane >> 4) * 8;
-      frag af[MB], bfr[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[i] = lfrag(base, wm * WM + i * 16 + (lane & 15), kel);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bfr[j] = lfrag(base, b_row_of(j), kel);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = E_::mma(af[i], bfr[j], acc[i][j]);
+      if (ks + 1 < KSUB) load_frags(base, ks + 1, (ks + 1) & 1);
+      mma_frags(ks & 1);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] per 16-row group
+  // ---- main loop: STAGES-deep LDS ring fed by DMA, one barrier per K tile --
+  // Step s: wait for this wave's loads of tile s, barrier (everyone's tile s
+  // has landed and everyone is done with tile s-1), refill the slot of tile
+  // s-1 with tile s+STAGES-1, multiply tile s.
+  const int nk = (int)(a.K / BK);
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue_stage(st, st);
+  int s = 0;
+  // steady state: STAGES-1 tiles are in flight at each wait
+  for (; s + STAGES - 1 < nk; ++s) {
+    wait_vm_barrier<(STAGES - 2) * SEG_PER_WAVE>();
+    issue_stage(s + STAGES - 1, (s + STAGES - 1) % STAGES);
+    compute(s % STAGES);
+  }
+  // drain: no more loads to issue
+  for (; s < nk; ++s) {
+    wait_vm_barrier<0>();
+    compute(s % STAGES);
+  }
+  __builtin_amdgcn_s_barrier();   // everyone is done reading the ring
+
+  // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] ------------------
+  // Each 16-row group has its own slot; a BS-row block holds BS/16 groups, so
+  // every distinct slot of the block gets its own pass with the rows of the
+  // other slots masked to zero.
   if (a.h != nullptr) {
-    int cached_l = -1;
-    frag bl[NB][2];   // up to RP = 64 -> two 32-deep steps
+    constexpr int NG = BS / 16;
+    constexpr int MAXKS = 64 / KF;   // RP <= 64
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int rloc = wm * WM + i * 16;
-      if (rloc >= nrows) continue;
-      const int64_t grow = row0 + rloc;
-      const int l = a.tile_lora[grow / a.BM_tile];
-      if (l < 0 || l >= a.L) continue;
-      const int r = min(a.lora_ranks[l], a.R);
-      if (r <= 0) continue;
-      const int nqs = (r + 31) / 32;
-      if (l != cached_l) {
-        cached_l = l;
+      const int rb = wm * WM + i * BS;
+      if (rb >= nrows) continue;
+      int lg[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int r16 = min(rb + 16 * g, nrows - 16);   // clamped: loads stay unconditional
+        const int l = a.tile_lora[(row0 + r16) / a.BM_tile];
+        const int lr = (l >= 0 && l < a.L) ? a.lora_ranks[l] : 0;
+        lg[g] = (rb + 16 * g < nrows && l >= 0 && l < a.L && lr > 0) ? l : -1;
+      }
+#pragma unroll
+      for (int pass = 0; pass < NG; ++pass) {
+        const int l = lg[pass];
+        if (l < 0) continue;
+        if (pass == 1 && lg[0] == l) continue;   // done together with group 0
+        const int r = min(a.lora_ranks[l], a.R);
+        const int nks = (r + KF - 1) / KF;
+        // rows of this lane's block row that belong to slot l; others read a
+        // valid row (the block's first) and are zeroed
+        const bool mine = lg[lrow / 16] == l;
+        const float* hrow = a.h + (row0 + rb + (mine ? lrow : 0)) * a.HS;
+        const T* pb[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const T* pool = a.b_pool0;
-          int cb = j;
-          if (GATE_UP && j >= NB / 2) { pool = a.b_pool1; cb = j - NB / 2; }
-          const int64_t col = n0 + (GATE_UP ? wn * (WN / 2) : wn * WN) + cb * 16 + (lane & 15);
-          const T* pbase = pool + (((int64_t)l * a.E + e) * a.R) * a.n_out + col;
-#pragma unroll
-          for (int qs = 0; qs < 2; ++qs) {
-            frag f = E_::zero();
-            if (qs < nqs && col < a.n_out) {
-#pragma unroll
-              for (int v = 0; v < 8; ++v) {
-                const int q = qs * 32 + (lane >> 4) * 8 + v;
-                if (q < r) f[v] = pbase[(int64_t)q * a.n_out];
-              }
-            }
-            bl[j][qs] = f;
-          }
+          const bool up = GATE_UP && j >= NB / 2;
+          const T* pool = up ? a.b_pool1 : a.b_pool0;
+          const int64_t col = min(col_of(j) + lrow, a.n_out - 1);
+          pb[j] = pool + (((int64_t)l * a.E + e) * a.R) * a.n_out + col;
         }
-      }
-      const float* hrow = a.h + (grow + (lane & 15)) * a.HS;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (qs >= nqs) continue;
-        const int q0 = qs * 32 + (lane >> 4) * 8;
-        const floatx8 hg = *reinterpret_cast<const floatx8*>(hrow + q0);
-        const floatx8 hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
-        if constexpr (sizeof(T) == 2) {
-          // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
-          frag g_hi, g_lo, u_hi, u_lo;
+        for (int ks = 0; ks < MAXKS; ++ks) {
+          if (ks >= nks) break;
+          const int q0 = ks * KF + lk;
+          floatx8 hg = *reinterpret_cast<const floatx8*>(hrow + q0);
+          floatx8 hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
+          // B^T rows q >= r are never read (q is clamped, the value zeroed)
+          frag bfv[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) bfv[j][v] = pb[j][(int64_t)min(q0 + v, r - 1) * a.n_out];
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            g_hi[v] = (bf16_t)hg[v];
-            g_lo[v] = (bf16_t)(hg[v] - (float)g_hi[v]);
-            u_hi[v] = (bf16_t)hu[v];
-            u_lo[v] = (bf16_t)(hu[v] - (float)u_hi[v]);
+            if (!mine) { hg[v] = 0.0f; hu[v] = 0.0f; }
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              if (q0 + v >= r || col_of(j) + lrow >= a.n_out) bfv[j][v] = E_::from_float(0.0f);
           }
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
             const bool up = GATE_UP && j >= NB / 2;
-            acc[i][j] = E_::mma(up ? u_hi : g_hi, bl[j][qs], acc[i][j]);
-            acc[i][j] = E_::mma(up ? u_lo : g_lo, bl[j][qs], acc[i][j]);
-          }
-        } else {
+            const floatx8& hv = up ? hu : hg;
+            if constexpr (sizeof(T) == 2) {
+              // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
+              frag hi, lo;
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const bool up = GATE_UP && j >= NB / 2;
-            acc[i][j] = E_::mma(up ? hu : hg, bl[j][qs], acc[i][j]);
+              for (int v = 0; v < 8; ++v) {
+                hi[v] = (bf16_t)hv[v];
+                lo[v] = (bf16_t)(hv[v] - (float)hi[v]);
+              }
+              acc[i][j] = B_::mma(hi, bfv[j], acc[i][j]);
+              acc[i][j] = B_::mma(lo, bfv[j], acc[i][j]);
+            } else {
+              acc[i][j] = B_::mma(hv, bfv[j], acc[i][j]);
+            }
           }
         }
       }
@@ -441,11 +568,11 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
       for (int j = 0; j < NB / 2; ++j) {
-        const int64_t col = n0 + wn * (WN / 2) + j * 16 + (lane & 15);
+        const int64_t col = col_of(j) + lrow;
         if (col >= a.n_out) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rloc = wm * WM + i * 16 + (lane >> 4) * 4 + v;
+        for (int v = 0; v < B_::ACC; ++v) {
+          const int rloc = wm * WM + i * BS + B_::row(v, lane);
           if (rloc >= nrows) continue;
           const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
           a.act[(row0 + rloc) * a.n_out + col] = E_::from_float(silu_f(g) * u);
@@ -456,21 +583,22 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rloc = wm * WM + i * 16 + (lane >> 4) * 4 + v;
-        if (rloc >= nrows) continue;
-        const int pid = a.sorted_ids[row0 + rloc];
-        if (pid >= a.P) continue;
-        const float wgt = a.topk_weights[pid];
+      for (int v = 0; v < B_::ACC; ++v) {
+        const int rloc = wm * WM + i * BS + B_::row(v, lane);
+        // clamped, unconditional loads so the compiler batches them
+        const int pid = a.sorted_ids[row0 + min(rloc, nrows - 1)];
+        const float wgt = a.topk_weights[min(pid, a.P - 1)];
+        if (rloc >= nrows || pid >= a.P) continue;
         float* zrow = a.z + (int64_t)pid * a.n_out;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
+          const int64_t col = col_of(j) + lrow;
           if (col < a.n_out) zrow[col] = wgt * acc[i][j][v];
         }
       }
     }
   }
+  }  // persistent tile loop
 }
 
 // --------------------------------------------------------------------------
@@ -495,8 +623,27 @@ combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, in
 // host side
 // --------------------------------------------------------------------------
 template <typename T> struct TileCfg;
-template <> struct TileCfg<bf16_t> { static constexpr int BM = 128, BN = 128; };
-template <> struct TileCfg<float> { static constexpr int BM = 64, BN = 64; };
+#ifndef MOELORA_BF16_BM
+#define MOELORA_BF16_BM 128
+#define MOELORA_BF16_BN 256
+#define MOELORA_BF16_WM 2
+#define MOELORA_BF16_WN 4
+#define MOELORA_BF16_STAGES 3
+#endif
+template <> struct TileCfg<bf16_t> {
+  static constexpr int BM = MOELORA_BF16_BM, BN = MOELORA_BF16_BN, WM = MOELORA_BF16_WM,
+                       WN = MOELORA_BF16_WN, STAGES = MOELORA_BF16_STAGES, PER_CU = 1;
+};
+template <> struct TileCfg<float> {
+  static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, PER_CU = 2;
+};
+
+// persistent GEMM grid: PER_CU workgroups on each of the 256 CUs, a multiple
+// of the 8 XCDs
+static int64_t gemm_grid(int64_t tiles, int per_cu) {
+  const int64_t full = 256 * per_cu;
+  return tiles >= full ? full : round_up(tiles > 0 ? tiles : 1, 8);
+}
 
 static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : TileCfg<float>::BM; }
 
@@ -565,7 +712,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hgu;
     s.cap = w.cap;
-    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)ceil_div(groups, 4)), dim3(256), 0,
+    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)groups), dim3(256), 0,
                        stream, s);
   }
   mark(2 * kStageShrinkX + 1);
@@ -598,9 +745,10 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool0 = static_cast<const T*>(p.b_gate);
     a.b_pool1 = static_cast<const T*>(p.b_up);
     a.act = act;
-    int64_t nblk = (int64_t)a.n_tiles * w.max_items;
+    int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, true>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, true>),
+                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageGateUp + 1);
   }
   mark(2 * kStageShrinkA);
@@ -622,7 +770,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hd;
     s.cap = w.cap;
-    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)ceil_div(groups, 4)), dim3(256), 0,
+    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)groups), dim3(256), 0,
                        stream, s);
   }
   mark(2 * kStageShrinkA + 1);
@@ -640,9 +788,10 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool0 = static_cast<const T*>(p.b_down);
     a.b_pool1 = nullptr;
     a.z = z;
-    int64_t nblk = (int64_t)a.n_tiles * w.max_items;
+    int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, false>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, false>),
+                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageDown + 1);
   }
   mark(2 * kStageCombine);
