@@ -40,7 +40,22 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit: "
+                         "the reference kernel that scales FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for counter calibration."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4}))
 
 
 class HipEvents:
@@ -156,6 +171,9 @@ def cpu_baseline(spec, inp, n_tokens):
 
 def main():
     args = parse()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the layer is TP=1 on a single MI355X and this build "

@@ -307,6 +307,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   static_assert(STAGES >= 2, "ring depth");
 
   __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+  __shared__ int ep_pid[BM];      // down epilogue: pair id of each tile row
+  __shared__ float ep_w[BM];      // and its router weight
 
   // Persistent tile loop.  Workgroups are dealt round-robin over the 8 XCDs;
   // each XCD owns a contiguous range of logical tiles and sweeps it in rounds
@@ -332,9 +334,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     continue;
   __syncthreads();  // the previous tile's last LDS reads are done
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = threadIdx.x >> 6;
+  // lane-derived values are recomputed per tile: the empty asm keeps the
+  // compiler from hoisting them out of the persistent loop, where they would
+  // stay live (and spill) across the main loop
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  (void)tid;
   const int lrow = lane % BS;                     // row / column this lane feeds
   const int lk = 8 * (lane / BS);                 // K offset of its 8 elements
 
@@ -444,11 +450,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 #pragma unroll
     for (int j = 0; j < NB; ++j) fb[set][j] = lfrag(base, b_row_of(j), kel);
   };
+  // row blocks wholly past nrows (a short last item of an expert) skip their
+  // MFMAs: the wave-uniform test leaves the SIMD to the other wave
   auto mma_frags = [&](int set) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i) {
+      if (wm * WM + i * BS >= nrows) continue;
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = B_::mma(fa[set][i], fb[set][j], acc[i][j]);
+    }
   };
   auto compute = [&](int buf) {
     const char* base = lds + buf * STAGE_BYTES;
@@ -580,15 +590,22 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       }
     }
   } else {
+    // pair ids and router weights of the tile's rows, staged once in LDS
+    for (int r = threadIdx.x; r < BM; r += 64 * NWAVES) {
+      const int pid = a.sorted_ids[row0 + min(r, nrows - 1)];
+      ep_pid[r] = r < nrows ? pid : a.P;
+      ep_w[r] = a.topk_weights[min(pid, a.P - 1)];
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
       for (int v = 0; v < B_::ACC; ++v) {
         const int rloc = wm * WM + i * BS + B_::row(v, lane);
-        // clamped, unconditional loads so the compiler batches them
-        const int pid = a.sorted_ids[row0 + min(rloc, nrows - 1)];
-        const float wgt = a.topk_weights[min(pid, a.P - 1)];
-        if (rloc >= nrows || pid >= a.P) continue;
+        if (rloc >= nrows) continue;
+        const int pid = ep_pid[rloc];
+        if (pid >= a.P) continue;
+        const float wgt = ep_w[rloc];
         float* zrow = a.z + (int64_t)pid * a.n_out;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
