@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace moelora {
 
 typedef __bf16 bf16_t;
@@ -73,5 +75,17 @@ __device__ inline float silu_f(float v) {
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.  Used
+// where an index selects accumulator registers, so the body is always
+// instantiated per index (never left as a runtime loop over a register array).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace moelora

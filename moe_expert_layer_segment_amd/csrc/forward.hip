@@ -499,10 +499,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   if (a.h != nullptr) {
     constexpr int NG = BS / 16;
     constexpr int MAXKS = 64 / KF;   // RP <= 64
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    static_for<MB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       const int rb = wm * WM + i * BS;
-      if (rb >= nrows) continue;
+      if (rb >= nrows) return;
       int lg[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
           }
         }
       }
-    }
+    });
   }
 
   // ---- epilogue -------------------------------------------------------------
