@@ -285,18 +285,21 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GATE_UP>
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int ROWB, bool GATE_UP>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T> a) {
   typedef Elt<T> E_;
   typedef Blk<T> B_;
   typedef typename E_::frag frag;
   typedef typename B_::acc_t acc_t;
   constexpr int BS = B_::BS, KF = B_::KF;
-  constexpr int ROWB = 128;                       // bytes per LDS tile row (one K tile)
-  constexpr int BK = ROWB / sizeof(T);            // 64 bf16 / 32 fp32
+  // ROWB: bytes per LDS tile row = one K tile of one row (64 or 128)
+  constexpr int BK = ROWB / sizeof(T);            // K elements per tile
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int RPS = 1024 / ROWB;                // rows per 1 KB DMA segment
+  static_assert(ROWB == 64 || ROWB == 128, "row size");
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int ROWS = BM + BN;                   // LDS rows per stage: A rows then B rows
-  constexpr int SEGS = ROWS / 8;                  // 1 KB segments (8 rows) per stage
+  constexpr int SEGS = ROWS / RPS;                // 1 KB segments per stage
   constexpr int SEG_PER_WAVE = SEGS / NWAVES;     // DMA instructions per wave per stage
   constexpr int STAGE_BYTES = ROWS * ROWB;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
@@ -355,7 +358,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // (l%8) ^ swz(row).  Rows outside the tile (pads, rows past nrows, columns
   // past n_out) load a valid row instead: MFMA rows / columns are
   // independent and those results are never stored.
-  auto swz = [](int row) -> int { return (row >> 1) & 7; };
+  // 16 lanes read 16 consecutive rows at one chunk: with 128-byte rows, rows
+  // 2 apart share banks, with 64-byte rows rows 4 apart
+  auto swz = [](int row) -> int {
+    return ROWB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  };
   const T* a_base = a.a_src;
   const T* b_base = a.w + (int64_t)e * a.w_rows * a.K;
   uint32_t src_off[SEG_PER_WAVE];   // byte offsets from a_base / b_base
@@ -364,15 +371,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     // pair ids of the gathered A rows: clamped, unconditional loads, issued together
 #pragma unroll
     for (int i = 0; i < SEG_PER_WAVE; ++i) {
-      const int row = (wave * SEG_PER_WAVE + i) * 8 + lane / 8;
+      const int row = (wave * SEG_PER_WAVE + i) * RPS + lane / CPR;
       pidv[i] = a.sorted_ids[row0 + min(min(row, BM - 1), nrows - 1)];
     }
   }
 #pragma unroll
   for (int i = 0; i < SEG_PER_WAVE; ++i) {
     const int seg = wave * SEG_PER_WAVE + i;
-    const int row = seg * 8 + lane / 8;
-    const int kc = (lane % 8) ^ swz(row);
+    const int row = seg * RPS + lane / CPR;
+    const int kc = (lane % CPR) ^ swz(row);
     int64_t grow;
     if (row < BM) {
       const int r = row;
@@ -399,7 +406,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 #pragma unroll
     for (int i = 0; i < SEG_PER_WAVE; ++i) {
       const int seg = wave * SEG_PER_WAVE + i;
-      const void* base = (seg * 8 < BM) ? (const void*)a_base : (const void*)b_base;
+      const void* base = (seg * RPS < BM) ? (const void*)a_base : (const void*)b_base;
       dma16(base, src_off[i] + kbytes, lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
   };
@@ -646,13 +653,15 @@ template <typename T> struct TileCfg;
 #define MOELORA_BF16_WM 2
 #define MOELORA_BF16_WN 4
 #define MOELORA_BF16_STAGES 3
+#define MOELORA_BF16_ROWB 128
 #endif
 template <> struct TileCfg<bf16_t> {
   static constexpr int BM = MOELORA_BF16_BM, BN = MOELORA_BF16_BN, WM = MOELORA_BF16_WM,
-                       WN = MOELORA_BF16_WN, STAGES = MOELORA_BF16_STAGES, PER_CU = 1;
+                       WN = MOELORA_BF16_WN, STAGES = MOELORA_BF16_STAGES,
+                       ROWB = MOELORA_BF16_ROWB, PER_CU = 1;
 };
 template <> struct TileCfg<float> {
-  static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, PER_CU = 2;
+  static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, ROWB = 128, PER_CU = 2;
 };
 
 // persistent GEMM grid: PER_CU workgroups on each of the 256 CUs, a multiple
@@ -764,7 +773,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.act = act;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, true>),
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
                        dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageGateUp + 1);
   }
@@ -807,7 +816,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.z = z;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, false>),
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, false>),
                        dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageDown + 1);
   }
