@@ -37,13 +37,93 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the batch the CPU oracle runs on (0: all of them)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
+                    help="repeat the oracle pass over the sample until this much time has passed")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: "
                          "the reference kernel that scales FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="host only: read the rocprofv3 counter CSVs under DIR/{fetch,write,"
+                         "cfetch,cwrite}, write the calibrated per-launch HBM traffic of every "
+                         "layer kernel of --config to --traffic and exit")
     return ap.parse_args()
+
+
+# kernel name (rocprofv3, mangled or not) -> forward stage or metadata kernel
+def _stage_of(kname):
+    if "gemm_kernel" in kname:
+        gate_up = ("Lb1E" in kname) or kname.rstrip(") ").split("(")[0].endswith("true>")
+        return "gate_up_gemm" if gate_up else "down_gemm"
+    if "shrink_kernel" in kname:
+        return "shrink_gate_up" if ("Li2E" in kname or ", 2>" in kname) else "shrink_down"
+    for key in ("combine", "plan", "info", "align_count", "align_scan", "align_scatter"):
+        if key + "_kernel" in kname:
+            return key
+    return None
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources and build script: counters taken on other code are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "moe_expert_layer_segment_amd")
+    csrc = os.path.join(pkg, "csrc")
+    for name in sorted(os.listdir(csrc)) + ["../build.py"]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes per launch, each scaled by what
+    the same counter reads for a plain copy of known size."""
+    import csv
+    import collections
+
+    def per_kernel(sub, counter):
+        path = os.path.join(args.traffic_from, sub, "run_counter_collection.csv")
+        agg = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    def copy_kib(d):
+        vals = [max(v) for k, v in d.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        assert vals, "no copy kernel in the calibration run"
+        return max(vals)
+
+    mib = 1024
+    f_scale = mib * 1024 / copy_kib(per_kernel("cfetch", "FETCH_SIZE"))
+    w_scale = mib * 1024 / copy_kib(per_kernel("cwrite", "WRITE_SIZE"))
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    stages = {}
+    for kname, vals in fetch.items():
+        st = _stage_of(kname)
+        if st is None:
+            continue
+        wv = write.get(kname, [0.0])
+        fb = float(np.mean(vals)) * f_scale * 1024
+        wb = float(np.mean(wv)) * w_scale * 1024
+        stages[st] = dict(bytes=round(fb + wb), fetch_bytes=round(fb), write_bytes=round(wb),
+                          dispatches=len(vals))
+    from moe_expert_layer_segment_amd import workloads
+    spec = workloads.config(args.config)
+    out = {}
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            out = json.load(f)
+    out[spec.name] = dict(stages=stages, fetch_scale=round(f_scale, 4),
+                          write_scale=round(w_scale, 4), copy_calibration_mib=mib,
+                          source_hash=kernel_source_hash())
+    with open(args.traffic, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out[spec.name]))
 
 
 def copy_calibration(mib):
@@ -123,13 +203,15 @@ def counts(spec, meta):
                 active_experts=int(len(active)), lora_buckets=len(buckets))
 
 
-def cpu_baseline(spec, inp, n_tokens):
-    """The oracle as it stands, on a bounded sample of the workload's tokens."""
+def cpu_baseline(spec, inp, n_tokens, min_seconds):
+    """The oracle as it stands, on a bounded sample of the workload's tokens, repeated
+    (at most 8 passes) until min_seconds have passed."""
     import oracle
     import torch
 
     T = spec.num_tokens
-    sample = np.unique(np.linspace(0, T - 1, min(n_tokens, T)).astype(np.int64))
+    n_tokens = T if n_tokens <= 0 else min(n_tokens, T)
+    sample = np.unique(np.linspace(0, T - 1, n_tokens).astype(np.int64))
     m = inp["meta"]
 
     class View:
@@ -151,11 +233,14 @@ def cpu_baseline(spec, inp, n_tokens):
     pools = {n: View(inp[n]) for n in ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
              if n in inp}
     t0 = time.perf_counter()
-    en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
-                                  m["max_seg_len"])
-    oracle.moe_lora_forward(XView(), m["topk_ids"], m["topk_weights"], View(inp["w_gate_up"]),
-                            View(inp["w_down"]), m["lora_ranks"], m["scaling"], mp, en,
-                            tokens=sample, **pools)
+    passes = 0
+    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
+                                      m["max_seg_len"])
+        oracle.moe_lora_forward(XView(), m["topk_ids"], m["topk_weights"],
+                                View(inp["w_gate_up"]), View(inp["w_down"]), m["lora_ranks"],
+                                m["scaling"], mp, en, tokens=sample, **pools)
+        passes += 1
     dt = time.perf_counter() - t0
     try:
         cores = len(os.sched_getaffinity(0))
@@ -164,13 +249,17 @@ def cpu_baseline(spec, inp, n_tokens):
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit():
         cores = min(cores, int(omp))
-    return dict(value=len(sample) / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{len(sample)} of {T} tokens (evenly spaced) of the same batch; float64 "
-                       f"numpy oracle incl. per-expert upcast of the touched weights; {dt:.1f} s")
+    return dict(value=passes * len(sample) / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{len(sample)} of {T} tokens (evenly spaced) of the same batch, "
+                       f"{passes} pass(es); float64 numpy oracle incl. per-expert upcast of the "
+                       f"touched weights; {dt:.1f} s")
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from_counters(args)
+        return
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
         return
@@ -250,9 +339,10 @@ def main():
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
-            tr = json.load(f).get(spec.name, {}).get("gate_up_gemm")
-        if tr:
-            traffic = tr
+            rec = json.load(f).get(spec.name, {})
+        # counters taken on other kernel code say nothing about this one
+        if rec.get("source_hash") == kernel_source_hash():
+            traffic = rec.get("stages", {}).get("gate_up_gemm", {}).get("bytes")
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=traffic,
                     kernel="gate_up_gemm", kernel_ms=round(gu_ms, 4),
@@ -261,7 +351,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(spec, inp, args.cpu_sample_tokens)
+        cpu = cpu_baseline(spec, inp, args.cpu_sample_tokens, args.cpu_min_seconds)
 
     tok_s = T / (ms * 1e-3)
     out = {
