@@ -337,7 +337,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     continue;
   __syncthreads();  // the previous tile's last LDS reads are done
 
-  const int wave = threadIdx.x >> 6;
+  // wave index in an SGPR: every wave-level test below is a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // lane-derived values are recomputed per tile: the empty asm keeps the
   // compiler from hoisting them out of the persistent loop, where they would
   // stay live (and spill) across the main loop
@@ -365,6 +366,23 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   };
   const T* a_base = a.a_src;
   const T* b_base = a.w + (int64_t)e * a.w_rows * a.K;
+  // global row (of a_base for row < BM, of b_base otherwise) behind LDS row `row`
+  auto grow_of = [&](int row, int pid_in) -> int64_t {
+    if (row < BM) {
+      const int r = row;
+      if (GATE_UP) {
+        const int pid = r < nrows ? pid_in : a.P;
+        return pid < a.P ? pid / a.top_k : 0;
+      }
+      return row0 + (r < nrows ? r : 0);
+    }
+    const int n = row - BM;
+    if (GATE_UP) {
+      const int64_t col = n0 + (n % (BN / 2));
+      return col < a.n_out ? ((n < BN / 2) ? col : a.n_out + col) : 0;
+    }
+    return n0 + n < a.n_out ? n0 + n : 0;
+  };
   uint32_t src_off[SEG_PER_WAVE];   // byte offsets from a_base / b_base
   int pidv[SEG_PER_WAVE];
   if (GATE_UP) {
@@ -380,35 +398,25 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     const int seg = wave * SEG_PER_WAVE + i;
     const int row = seg * RPS + lane / CPR;
     const int kc = (lane % CPR) ^ swz(row);
-    int64_t grow;
-    if (row < BM) {
-      const int r = row;
-      if (GATE_UP) {
-        const int pid = r < nrows ? pidv[i] : a.P;
-        grow = pid < a.P ? pid / a.top_k : 0;
-      } else {
-        grow = row0 + (r < nrows ? r : 0);
-      }
-    } else {
-      const int n = row - BM;
-      if (GATE_UP) {
-        const int64_t col = n0 + (n % (BN / 2));
-        grow = col < a.n_out ? ((n < BN / 2) ? col : a.n_out + col) : 0;
-      } else {
-        grow = n0 + n < a.n_out ? n0 + n : 0;
-      }
-    }
-    src_off[i] = (uint32_t)((grow * a.K + kc * E_::kChunk) * sizeof(T));
+    src_off[i] = (uint32_t)((grow_of(row, pidv[i]) * a.K + kc * E_::kChunk) * sizeof(T));
   }
+
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  auto issue_stage = [&](int stage_k, int buf) {
+  // this wave's DMA instructions [I0, I1) of one stage
+  auto issue_part = [&](auto i0_c, auto i1_c, int stage_k, int buf) {
+    constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
     const uint32_t kbytes = (uint32_t)stage_k * ROWB;
 #pragma unroll
-    for (int i = 0; i < SEG_PER_WAVE; ++i) {
+    for (int i = I0; i < I1; ++i) {
       const int seg = wave * SEG_PER_WAVE + i;
       const void* base = (seg * RPS < BM) ? (const void*)a_base : (const void*)b_base;
       dma16(base, src_off[i] + kbytes, lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
+  };
+  const int nk = (int)(a.K / BK);
+  auto issue_stage = [&](int stage_k, int buf) {
+    issue_part(std::integral_constant<int, 0>{}, std::integral_constant<int, SEG_PER_WAVE>{},
+               stage_k, buf);
   };
   // one frag (8 K elements starting at kel) of LDS row `row`
   auto lfrag = [&](const char* base, int row, int kel) -> frag {
@@ -457,46 +465,67 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 #pragma unroll
     for (int j = 0; j < NB; ++j) fb[set][j] = lfrag(base, b_row_of(j), kel);
   };
-  // row blocks wholly past nrows (a short last item of an expert) skip their
-  // MFMAs: the wave-uniform test leaves the SIMD to the other wave
-  auto mma_frags = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      if (wm * WM + i * BS >= nrows) continue;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = B_::mma(fa[set][i], fb[set][j], acc[i][j]);
-    }
-  };
-  auto compute = [&](int buf) {
-    const char* base = lds + buf * STAGE_BYTES;
-    load_frags(base, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < KSUB; ++ks) {
-      if (ks + 1 < KSUB) load_frags(base, ks + 1, (ks + 1) & 1);
-      mma_frags(ks & 1);
-    }
-  };
-
   // ---- main loop: STAGES-deep LDS ring fed by DMA, one barrier per K tile --
   // Step s: wait for this wave's loads of tile s, barrier (everyone's tile s
   // has landed and everyone is done with tile s-1), refill the slot of tile
   // s-1 with tile s+STAGES-1, multiply tile s.
-  const int nk = (int)(a.K / BK);
+  //
+  // The loop is instantiated twice: with every row block of the wave live
+  // (no test near the MFMAs, so the compiler interleaves them freely with
+  // the LDS reads), and for a short last item of an expert, where row blocks
+  // wholly past nrows skip their MFMAs (a scalar test: the wave index is
+  // uniform).
+  auto main_loop = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    auto mma_frags = [&](int set) {
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nk) issue_stage(st, st);
-  int s = 0;
-  // steady state: STAGES-1 tiles are in flight at each wait
-  for (; s + STAGES - 1 < nk; ++s) {
-    wait_vm_barrier<(STAGES - 2) * SEG_PER_WAVE>();
-    issue_stage(s + STAGES - 1, (s + STAGES - 1) % STAGES);
-    compute(s % STAGES);
-  }
-  // drain: no more loads to issue
-  for (; s < nk; ++s) {
-    wait_vm_barrier<0>();
-    compute(s % STAGES);
-  }
+      for (int i = 0; i < MB; ++i) {
+        if (!FULL && wm * WM + i * BS >= nrows) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = B_::mma(fa[set][i], fb[set][j], acc[i][j]);
+      }
+    };
+    // Multiply the stage in ring slot buf; when next_k >= 0 also issue the
+    // DMA of K tile next_k into slot next_buf, spread over the sub-steps.
+    // Instruction order is pinned with scheduling barriers: the fragment
+    // reads of sub-step ks+1 and a share of the DMA go out before the MFMAs
+    // of sub-step ks, so LDS latency and DMA issue hide behind MFMA work.
+    auto compute = [&](int buf, int next_k, int next_buf) {
+      const char* base = lds + buf * STAGE_BYTES;
+      load_frags(base, 0, 0);
+      static_for<KSUB>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        constexpr int d0 = ks * SEG_PER_WAVE / KSUB, d1 = (ks + 1) * SEG_PER_WAVE / KSUB;
+        __builtin_amdgcn_sched_barrier(0);
+        if (next_k >= 0)
+          issue_part(std::integral_constant<int, d0>{}, std::integral_constant<int, d1>{},
+                     next_k, next_buf);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 1 < KSUB) load_frags(base, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags(ks & 1);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nk) issue_stage(st, st);
+    int s = 0;
+    // steady state: STAGES-1 tiles are in flight at each wait
+    for (; s + STAGES - 1 < nk; ++s) {
+      wait_vm_barrier<(STAGES - 2) * SEG_PER_WAVE>();
+      compute(s % STAGES, s + STAGES - 1, (s + STAGES - 1) % STAGES);
+    }
+    // drain: no more loads to issue
+    for (; s < nk; ++s) {
+      wait_vm_barrier<0>();
+      compute(s % STAGES, -1, 0);
+    }
+  };
+  if (wm * WM + WM <= nrows)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   __builtin_amdgcn_s_barrier();   // everyone is done reading the ring
 
   // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] ------------------
