@@ -65,6 +65,8 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
     }
   }
   if (threadIdx.x == 0) item_count[0] = min(lds_waves[kPlanThreads / 64], max_items);
+  // the two GEMMs' per-XCD tile counters follow the item count
+  if (threadIdx.x < 16) item_count[4 + threadIdx.x] = 0;
 }
 
 // --------------------------------------------------------------------------
@@ -238,6 +240,7 @@ struct GemmArgs {
   float* z;                   // down: [P, n_out]
   const float* topk_weights;
   int64_t cap;                // rows of sorted_ids / act / h
+  int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
 };
 
 #ifndef MOELORA_GROUP_M
@@ -314,27 +317,35 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   __shared__ float ep_w[BM];      // and its router weight
 
   // Persistent tile loop.  Workgroups are dealt round-robin over the 8 XCDs;
-  // each XCD owns a contiguous range of logical tiles and sweeps it in rounds
-  // of (its workgroups) tiles, so the tiles resident on one XCD at a time are
-  // neighbours: kGroupM work items x consecutive column tiles, sharing x rows
-  // and weight columns in that XCD's L2.
+  // each XCD owns a contiguous range of logical tiles, handed out in order by
+  // a per-XCD counter, so the tiles resident on one XCD at any time are a
+  // sliding window of neighbours (kGroupM work items x consecutive column
+  // tiles) sharing x rows and weight columns in that XCD's L2.  A workgroup
+  // claims its next tile when it starts the current one.
   const int count = min(a.item_count[0], a.max_items);
   const int total = (int)ceil_div(count, kGroupM) * kGroupM * a.n_tiles;
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_round = gridDim.x / 8;
+  const int xcd = blockIdx.x % 8;
   const int per_xcd = (total + 7) / 8;
   const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
   const int per_group = kGroupM * a.n_tiles;
-  for (int logical = t_begin + slot; logical < t_end; logical += per_round) {
+  __shared__ int claimed;
+  if (threadIdx.x == 0) claimed = atomicAdd(&a.tile_ctr[xcd], 1);
+  __syncthreads();
+  int logical = t_begin + claimed;
+  while (logical < t_end) {
+  int next_claim = 0;
+  if (threadIdx.x == 0) next_claim = atomicAdd(&a.tile_ctr[xcd], 1);
+  [&]() {
   const int item_idx = (logical / per_group) * kGroupM + (logical % per_group) % kGroupM;
   const int ntile = (logical % per_group) / kGroupM;
-  if (item_idx >= count || ntile >= a.n_tiles) continue;
+  if (item_idx >= count || ntile >= a.n_tiles) return;
   const int4 item = a.items[item_idx];
   const int64_t row0 = item.x;
   const int nrows = item.y;
   const int e = item.z;
   if (row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) || (row0 & 15) || row0 + nrows > a.cap ||
       e < 0 || e >= a.E)
-    continue;
+    return;
   __syncthreads();  // the previous tile's last LDS reads are done
 
   // wave index in an SGPR: every wave-level test below is a scalar branch
@@ -651,6 +662,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       }
     }
   }
+  }();
+  __syncthreads();   // everyone has read the current claim
+  if (threadIdx.x == 0) claimed = next_claim;
+  __syncthreads();
+  logical = t_begin + claimed;
   }  // persistent tile loop
 }
 
@@ -714,7 +730,7 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
-  w.count_off = take(sizeof(int32_t) * 4);
+  w.count_off = take(sizeof(int32_t) * 20);   // item count, then 2 x 8 tile counters
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * w.RP : 0);
@@ -800,6 +816,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool0 = static_cast<const T*>(p.b_gate);
     a.b_pool1 = static_cast<const T*>(p.b_up);
     a.act = act;
+    a.tile_ctr = count + 4;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
@@ -843,6 +860,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool0 = static_cast<const T*>(p.b_down);
     a.b_pool1 = nullptr;
     a.z = z;
+    a.tile_ctr = count + 12;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, false>),
