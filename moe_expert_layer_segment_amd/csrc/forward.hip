@@ -694,10 +694,20 @@ combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, in
 template <typename T> struct TileCfg;
 #ifndef MOELORA_BF16_BM
 #define MOELORA_BF16_BM 128
+#endif
+#ifndef MOELORA_BF16_BN
 #define MOELORA_BF16_BN 256
+#endif
+#ifndef MOELORA_BF16_WM
 #define MOELORA_BF16_WM 2
+#endif
+#ifndef MOELORA_BF16_WN
 #define MOELORA_BF16_WN 4
+#endif
+#ifndef MOELORA_BF16_STAGES
 #define MOELORA_BF16_STAGES 3
+#endif
+#ifndef MOELORA_BF16_ROWB
 #define MOELORA_BF16_ROWB 128
 #endif
 template <> struct TileCfg<bf16_t> {
