@@ -71,7 +71,9 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
 
 // --------------------------------------------------------------------------
 // shrink: h[row, pool*RP + q] = s_l * sum_k a_src[row, k] * A_pool[l, e, q, k]
-// for q < r_l (zero for r_l <= q < RP).  One wave per 16-row group.
+// for q < r_l (zero for r_l <= q < RP).  One workgroup per (16-row group, K
+// split); with more than one split, split c writes its partial sums to its
+// own buffer and shrink_reduce adds them, in split order, into split 0.
 // --------------------------------------------------------------------------
 template <typename T>
 struct ShrinkArgs {
@@ -79,6 +81,8 @@ struct ShrinkArgs {
   const int32_t* sorted_ids;  // gathered mode: pair id of each row
   int gathered, top_k, P;
   int64_t K;                  // contraction length (H or I)
+  int64_t kchunk;             // K elements per split (multiple of 128)
+  int64_t split_stride;       // floats between the splits' h buffers
   const T* pool0;             // [L, E, R, K]
   const T* pool1;             // second pool or null
   int R, RP, L, E, BM;
@@ -102,6 +106,8 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   if (row0 >= a.num_rows_padded[0] || row0 + 16 > a.cap) return;
+  const int64_t k_begin = (int64_t)blockIdx.y * a.kchunk;
+  const int64_t k_end = min(a.K, k_begin + a.kchunk);
   const int tile = (int)(row0 / a.BM);
   const int l = a.tile_lora[tile];
   if (l < 0 || l >= a.L) return;
@@ -110,7 +116,7 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
   const int r = min(a.lora_ranks[l], a.R);
   const float s = a.scaling[l];
   const int HS = NPOOL * a.RP;
-  float* hrow_base = a.h + row0 * HS;
+  float* hrow_base = a.h + (int64_t)blockIdx.y * a.split_stride + row0 * HS;
   if (r <= 0) {
     // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
     for (int i = threadIdx.x; i < 16 * HS; i += 256) hrow_base[i] = 0.0f;
@@ -147,7 +153,7 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
     for (int qb = 0; qb < NQB; ++qb) acc[pi][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 2
-  for (int64_t k0 = wave * 32; k0 < a.K; k0 += 128) {
+  for (int64_t k0 = k_begin + wave * 32; k0 < k_end; k0 += 128) {
     frag av = arow ? load_frag_global<T>(arow + k0 + kq) : E_::zero();
 #pragma unroll
     for (int pi = 0; pi < NPOOL; ++pi)
@@ -184,6 +190,17 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
         hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
       }
     }
+}
+
+// h[0] += h[1] + ... + h[S-1] over the padded rows, in split order
+__global__ void __launch_bounds__(256)
+shrink_reduce_kernel(float* __restrict__ h, int64_t split_stride, int splits,
+                     const int32_t* __restrict__ num_rows_padded, int HS) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)num_rows_padded[0] * HS) return;
+  floatx4 v = *reinterpret_cast<const floatx4*>(h + i);
+  for (int sp = 1; sp < splits; ++sp) v += *reinterpret_cast<const floatx4*>(h + sp * split_stride + i);
+  *reinterpret_cast<floatx4*>(h + i) = v;
 }
 
 // --------------------------------------------------------------------------
@@ -728,6 +745,17 @@ static int64_t gemm_grid(int64_t tiles, int per_cu) {
 
 static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : TileCfg<float>::BM; }
 
+// K splits of a shrink: enough workgroups to fill the GPU when the batch has
+// few rows (decode), each split at least 512 deep and a multiple of 128 (the
+// four waves' interleaved 32-deep steps).
+static int64_t shrink_kchunk(int64_t P, int64_t K) {
+  const int64_t groups = P / 16 + 1;
+  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(1024, groups)));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
+  return round_up(ceil_div(K, s), 128);
+}
+static int shrink_splits(int64_t P, int64_t K) { return (int)ceil_div(K, shrink_kchunk(P, K)); }
+
 ForwardWs forward_ws_layout(const ForwardProblem& p) {
   ForwardWs w;
   const int64_t P = p.T * p.k;
@@ -741,9 +769,11 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
   w.count_off = take(sizeof(int32_t) * 20);   // item count, then 2 x 8 tile counters
-  w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * 2 * w.RP : 0);
+  w.split_gu = shrink_splits(p.T * p.k, p.H);
+  w.split_d = shrink_splits(p.T * p.k, p.I);
+  w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
-  w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.cap * w.RP : 0);
+  w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
   w.z_off = take(sizeof(float) * (size_t)P * p.H);
   w.bytes = off;
   return w;
@@ -793,8 +823,14 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hgu;
     s.cap = w.cap;
-    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)groups), dim3(256), 0,
-                       stream, s);
+    s.kchunk = shrink_kchunk(P, p.H);
+    s.split_stride = w.cap * 2 * w.RP;
+    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)groups, (unsigned)w.split_gu),
+                       dim3(256), 0, stream, s);
+    if (w.split_gu > 1)
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * 2 * w.RP / 4, 256)),
+                         dim3(256), 0, stream, hgu, (int64_t)s.split_stride, w.split_gu,
+                         p.num_rows_padded, (int)(2 * w.RP));
   }
   mark(2 * kStageShrinkX + 1);
 
@@ -852,8 +888,14 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hd;
     s.cap = w.cap;
-    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)groups), dim3(256), 0,
-                       stream, s);
+    s.kchunk = shrink_kchunk(P, p.I);
+    s.split_stride = w.cap * w.RP;
+    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)groups, (unsigned)w.split_d),
+                       dim3(256), 0, stream, s);
+    if (w.split_d > 1)
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.RP / 4, 256)),
+                         dim3(256), 0, stream, hd, (int64_t)s.split_stride, w.split_d,
+                         p.num_rows_padded, (int)w.RP);
   }
   mark(2 * kStageShrinkA + 1);
   // down

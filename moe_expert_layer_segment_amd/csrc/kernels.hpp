@@ -53,6 +53,7 @@ struct ForwardProblem {
 struct ForwardWs {
   int64_t cap, max_items, RP;
   size_t items_off, count_off, hgu_off, act_off, hd_off, z_off, bytes;
+  int split_gu = 1, split_d = 1;   // K splits of the two shrinks
 };
 ForwardWs forward_ws_layout(const ForwardProblem& p);
 // stages of the forward, in launch order (index into the optional event pairs)
