@@ -727,13 +727,21 @@ template <typename T> struct TileCfg;
 #ifndef MOELORA_BF16_ROWB
 #define MOELORA_BF16_ROWB 128
 #endif
+#ifndef MOELORA_BF16_BN_DOWN
+#define MOELORA_BF16_BN_DOWN MOELORA_BF16_BN
+#endif
+#ifndef MOELORA_BF16_STAGES_DOWN
+#define MOELORA_BF16_STAGES_DOWN MOELORA_BF16_STAGES
+#endif
 template <> struct TileCfg<bf16_t> {
   static constexpr int BM = MOELORA_BF16_BM, BN = MOELORA_BF16_BN, WM = MOELORA_BF16_WM,
                        WN = MOELORA_BF16_WN, STAGES = MOELORA_BF16_STAGES,
                        ROWB = MOELORA_BF16_ROWB, PER_CU = 1;
+  static constexpr int BN_DOWN = MOELORA_BF16_BN_DOWN, STAGES_DOWN = MOELORA_BF16_STAGES_DOWN;
 };
 template <> struct TileCfg<float> {
   static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, ROWB = 128, PER_CU = 2;
+  static constexpr int BN_DOWN = 64, STAGES_DOWN = 3;
 };
 
 // persistent GEMM grid: PER_CU workgroups on each of the 256 CUs, a multiple
@@ -906,7 +914,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.w = static_cast<const T*>(p.w_down);
     a.n_out = p.H;
     a.w_rows = p.H;
-    a.n_tiles = (int)ceil_div(p.H, BN);
+    constexpr int BND = TileCfg<T>::BN_DOWN, SD = TileCfg<T>::STAGES_DOWN;
+    a.n_tiles = (int)ceil_div(p.H, BND);
     a.h = lora ? hd : nullptr;
     a.HS = (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b_down);
@@ -915,7 +924,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.tile_ctr = count + 12;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, false>),
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
                        dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageDown + 1);
   }
