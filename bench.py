@@ -58,6 +58,8 @@ def _stage_of(kname):
     if "gemm_kernel" in kname:
         gate_up = ("Lb1E" in kname) or kname.rstrip(") ").split("(")[0].endswith("true>")
         return "gate_up_gemm" if gate_up else "down_gemm"
+    if "shrink_reduce" in kname:
+        return "shrink_reduce"
     if "shrink_kernel" in kname:
         return "shrink_gate_up" if ("Li2E" in kname or ", 2>" in kname) else "shrink_down"
     for key in ("combine", "plan", "info", "align_count", "align_scan", "align_scatter"):
