@@ -637,21 +637,33 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   }
 
   // ---- epilogue -------------------------------------------------------------
+  // Results go through this wave's own LDS region (the ring is idle after the
+  // barrier that ended the K loop) so that every lane stores 16 contiguous
+  // bytes: a lane's accumulators hold one column of several rows.
+  constexpr int CH = 16 / (GATE_UP ? (int)sizeof(T) : 4);   // elements per 16-byte chunk
   if (GATE_UP) {
+    // act = SiLU(gate) * up, [WM rows][WN/2 cols] of T per wave
+    constexpr int EW = WN / 2;
+    static_assert(NWAVES * WM * EW * sizeof(T) <= STAGES * STAGE_BYTES, "epilogue staging fits");
+    T* ep = reinterpret_cast<T*>(lds) + wave * (WM * EW);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB / 2; ++j) {
-        const int64_t col = col_of(j) + lrow;
-        if (col >= a.n_out) continue;
+      for (int j = 0; j < NB / 2; ++j)
 #pragma unroll
         for (int v = 0; v < B_::ACC; ++v) {
-          const int rloc = wm * WM + i * BS + B_::row(v, lane);
-          if (rloc >= nrows) continue;
           const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
-          a.act[(row0 + rloc) * a.n_out + col] = E_::from_float(silu_f(g) * u);
+          ep[(i * BS + B_::row(v, lane)) * EW + j * BS + lrow] = E_::from_float(silu_f(g) * u);
         }
-      }
+    constexpr int CPRW = EW / CH;   // chunks per row
+#pragma unroll
+    for (int c = lane; c < WM * CPRW; c += 64) {
+      const int r = c / CPRW, cc = c % CPRW;
+      const int rloc = wm * WM + r;
+      const int64_t col = n0 + wn * EW + cc * CH;
+      if (rloc >= nrows || col >= a.n_out) continue;
+      const int4v vv = *reinterpret_cast<const int4v*>(ep + r * EW + cc * CH);
+      *reinterpret_cast<int4v*>(a.act + (row0 + rloc) * a.n_out + col) = vv;
     }
   } else {
     // pair ids and router weights of the tile's rows, staged once in LDS
@@ -660,23 +672,31 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       ep_pid[r] = r < nrows ? pid : a.P;
       ep_w[r] = a.topk_weights[min(pid, a.P - 1)];
     }
-    __syncthreads();
+    // the unweighted results, [WM rows][WN cols] fp32 per wave
+    static_assert(NWAVES * WM * WN * 4 <= STAGES * STAGE_BYTES, "epilogue staging fits");
+    float* ep = reinterpret_cast<float*>(lds) + wave * (WM * WN);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int v = 0; v < B_::ACC; ++v) {
-        const int rloc = wm * WM + i * BS + B_::row(v, lane);
-        if (rloc >= nrows) continue;
-        const int pid = ep_pid[rloc];
-        if (pid >= a.P) continue;
-        const float wgt = ep_w[rloc];
-        float* zrow = a.z + (int64_t)pid * a.n_out;
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int64_t col = col_of(j) + lrow;
-          if (col < a.n_out) zrow[col] = wgt * acc[i][j][v];
-        }
-      }
+        for (int v = 0; v < B_::ACC; ++v)
+          ep[(i * BS + B_::row(v, lane)) * WN + j * BS + lrow] = acc[i][j][v];
+    __syncthreads();   // ep_pid / ep_w are written by other waves
+    constexpr int CPRW = WN / CH;
+#pragma unroll 4
+    for (int c = lane; c < WM * CPRW; c += 64) {
+      const int r = c / CPRW, cc = c % CPRW;
+      const int rloc = wm * WM + r;
+      const int64_t col = n0 + wn * WN + cc * CH;
+      if (rloc >= nrows || col >= a.n_out) continue;
+      const int pid = ep_pid[rloc];
+      if (pid >= a.P) continue;
+      const float wgt = ep_w[rloc];
+      floatx4 vv = *reinterpret_cast<const floatx4*>(ep + r * WN + cc * CH);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vv[q] = wgt * vv[q];
+      *reinterpret_cast<floatx4*>(a.z + (int64_t)pid * a.n_out + col) = vv;
     }
   }
   }();
