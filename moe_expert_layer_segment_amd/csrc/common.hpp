@@ -67,11 +67,12 @@ __device__ inline typename Elt<T>::frag load_frag_global(const T* p) {
 }
 
 // SiLU(v) = v * sigmoid(v) = v / (1 + e^-v), with e^-v evaluated as
-// 2^(-v * log2(e)) on the hardware exp2 unit.
+// 2^(-v * log2(e)) on the hardware exp2 unit and the division as a multiply
+// by the hardware reciprocal (about 1 ulp; for e^-v = inf it gives 0).
 __device__ inline float silu_f(float v) {
   const float kLog2e = 1.4426950408889634f;
   float e = __builtin_amdgcn_exp2f(-v * kLog2e);
-  return v / (1.0f + e);
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
