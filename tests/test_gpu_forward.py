@@ -147,7 +147,7 @@ def test_determinism_and_block_m_invariance():
     y1 = run(inp).clone()
     y2 = run(inp).clone()
     assert torch.equal(y1, y2)
-    for bm in (32, 64, 128):
+    for bm in (32, 64, 128, 256):
         assert torch.equal(run(inp, block_m=bm), y1), bm
 
 
