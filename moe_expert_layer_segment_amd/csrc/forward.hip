@@ -59,8 +59,9 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
   for (int e = e0; e < e1; ++e) {
     int row0 = expert_tile_offsets[e] * BM;
     int rows = (expert_tile_offsets[e + 1] - expert_tile_offsets[e]) * BM;
+    const int first = start;   // the expert's first item: the GEMMs order tiles by expert
     for (int r = 0; r < rows; r += rows_per_item) {
-      if (start < max_items) items[start] = make_int4(row0 + r, min(rows_per_item, rows - r), e, 0);
+      if (start < max_items) items[start] = make_int4(row0 + r, min(rows_per_item, rows - r), e, first);
       ++start;
     }
   }
@@ -246,6 +247,7 @@ struct GemmArgs {
   int64_t w_rows;             // rows per expert of w (2I or H)
   // LoRA
   const int32_t* tile_lora;
+  const int32_t* expert_tile_offsets;   // [E+1], in align blocks of BM_tile rows
   int BM_tile;
   const int32_t* lora_ranks;
   const float* h;             // [cap, HS], fp32 (scaled shrink result)
@@ -260,10 +262,6 @@ struct GemmArgs {
   int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
 };
 
-#ifndef MOELORA_GROUP_M
-#define MOELORA_GROUP_M 8
-#endif
-static constexpr int kGroupM = MOELORA_GROUP_M;  // work items per tile-order group
 
 __device__ inline int xcd_remap(int bid, int nblocks) {
   // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
@@ -333,18 +331,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   __shared__ int ep_pid[BM];      // down epilogue: pair id of each tile row
   __shared__ float ep_w[BM];      // and its router weight
 
-  // Persistent tile loop.  Workgroups are dealt round-robin over the 8 XCDs;
-  // each XCD owns a contiguous range of logical tiles, handed out in order by
-  // a per-XCD counter, so the tiles resident on one XCD at any time are a
-  // sliding window of neighbours (kGroupM work items x consecutive column
-  // tiles) sharing x rows and weight columns in that XCD's L2.  A workgroup
-  // claims its next tile when it starts the current one.
+  // Persistent tile loop.  Logical tiles are ordered expert by expert, and
+  // inside an expert by groups of its work items, column-major with the
+  // group's items fastest, so a weight column tile is fetched once per group
+  // and shared by its items.  Workgroups are dealt round-robin over the 8 XCDs; each XCD owns a
+  // contiguous range of logical tiles, handed out in order by a per-XCD
+  // counter, so the tiles resident on one XCD at any time are a sliding
+  // window of neighbours sharing x rows and weight columns in its L2.  A
+  // workgroup claims its next tile when it starts the current one.
   const int count = min(a.item_count[0], a.max_items);
-  const int total = (int)ceil_div(count, kGroupM) * kGroupM * a.n_tiles;
+  const int total = count * a.n_tiles;
   const int xcd = blockIdx.x % 8;
   const int per_xcd = (total + 7) / 8;
   const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
-  const int per_group = kGroupM * a.n_tiles;
   __shared__ int claimed;
   if (threadIdx.x == 0) claimed = atomicAdd(&a.tile_ctr[xcd], 1);
   __syncthreads();
@@ -353,8 +352,27 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   int next_claim = 0;
   if (threadIdx.x == 0) next_claim = atomicAdd(&a.tile_ctr[xcd], 1);
   [&]() {
-  const int item_idx = (logical / per_group) * kGroupM + (logical % per_group) % kGroupM;
-  const int ntile = (logical % per_group) / kGroupM;
+  // the expert group of logical tile `logical` spans its items' range times
+  // n_tiles, so item logical / n_tiles belongs to it
+  const int4 in_group = a.items[logical / a.n_tiles];
+  const int first = in_group.w, eg = in_group.z;
+  if (eg < 0 || eg >= a.E || first < 0 || first > logical / a.n_tiles) return;
+  const int rows_e = (a.expert_tile_offsets[eg + 1] - a.expert_tile_offsets[eg]) * a.BM_tile;
+  const int n_e = (rows_e + BM - 1) / BM;   // the expert's items
+  if (n_e <= 0) return;
+  // The expert's items are cut into round(n_e / 8) near-equal groups; a
+  // group's tiles are column-major, its items fastest.  (About 8 items per
+  // group balances the x rows and the weight columns a window of 32 resident
+  // tiles fetches: a 128-row x tile is half a 256-row weight tile.)
+  const int ng = max(1, (n_e + 4) / 8);
+  const int gbase = n_e / ng, grem = n_e % ng;   // groups 0..grem-1 have gbase+1 items
+  const int li = logical / a.n_tiles - first;    // an item index inside the group
+  const int gj = li < grem * (gbase + 1) ? li / (gbase + 1) : grem + (li - grem * (gbase + 1)) / gbase;
+  const int g_off = gj * gbase + min(gj, grem);  // the group's first item
+  const int g_n = gbase + (gj < grem ? 1 : 0);
+  const int local = logical - (first + g_off) * a.n_tiles;
+  const int item_idx = first + g_off + local % g_n;
+  const int ntile = local / g_n;
   if (item_idx >= count || ntile >= a.n_tiles) return;
   const int4 item = a.items[item_idx];
   const int64_t row0 = item.x;
@@ -870,6 +888,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   g.P = (int)P;
   g.sorted_ids = p.sorted_ids;
   g.tile_lora = p.tile_lora;
+  g.expert_tile_offsets = p.expert_tile_offsets;
   g.BM_tile = (int)p.BM;
   g.lora_ranks = p.lora_ranks;
   g.RP = (int)w.RP; g.R = (int)p.R; g.L = (int)p.L; g.E = (int)p.E;
@@ -891,7 +910,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool1 = static_cast<const T*>(p.b_up);
     a.act = act;
     a.tile_ctr = count + 4;
-    int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
+    int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
                        dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
@@ -942,7 +961,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.b_pool1 = nullptr;
     a.z = z;
     a.tile_ctr = count + 12;
-    int64_t nblk = gemm_grid((int64_t)a.n_tiles * ceil_div(w.max_items, kGroupM) * kGroupM, TileCfg<T>::PER_CU);
+    int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
     hipLaunchKernelGGL((gemm_kernel<T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
                        dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
