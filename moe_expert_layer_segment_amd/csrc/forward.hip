@@ -347,10 +347,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   __shared__ int claimed;
   if (threadIdx.x == 0) claimed = atomicAdd(&a.tile_ctr[xcd], 1);
   __syncthreads();
-  int logical = t_begin + claimed;
+  int logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);   // uniform: scalar loads of the tile's metadata
   while (logical < t_end) {
   int next_claim = 0;
   if (threadIdx.x == 0) next_claim = atomicAdd(&a.tile_ctr[xcd], 1);
+  bool published = false;   // the next claim was written to LDS inside the tile
   [&]() {
   // the expert group of logical tile `logical` spans its items' range times
   // n_tiles, so item logical / n_tiles belongs to it
@@ -446,6 +447,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     const int kc = (lane % CPR) ^ swz(row);
     src_off[i] = (uint32_t)((grow_of(row, pidv[i]) * a.K + kc * E_::kChunk) * sizeof(T));
   }
+  // Publish the next claim now: every wave read the current one before the
+  // barrier above, and the K loop's barriers make this write visible before
+  // the end of the tile.  (The claim's load has completed: the pair-id loads
+  // issued after it were just waited for.)
+  if (threadIdx.x == 0) claimed = next_claim;
+  published = true;
 
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   // this wave's DMA instructions [I0, I1) of one stage
@@ -500,6 +507,32 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < B_::ACC; ++v) acc[i][j][v] = 0.0f;
+
+  // LoRA slot table of this wave's row blocks, read before the K loop so the
+  // expand after it does not wait on these dependent loads: lg[i][g] = slot
+  // of 16-row group g of block i (-1: none or rank 0); p0[i] = slot of the
+  // block's first pass (its first served group), r0[i] its rank.
+  constexpr int NG = BS / 16;
+  int lg[MB][NG], p0[MB], r0[MB];
+  if (a.h != nullptr) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int rb = wm * WM + i * BS;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int r16 = max(min(rb + 16 * g, nrows - 16), 0);   // clamped: loads stay unconditional
+        const int l = a.tile_lora[(row0 + r16) / a.BM_tile];
+        const int lr = (l >= 0 && l < a.L) ? a.lora_ranks[l] : 0;
+        lg[i][g] = (rb + 16 * g < nrows && l >= 0 && l < a.L && lr > 0) ? l : -1;
+      }
+      int l = -1;
+#pragma unroll
+      for (int g = NG - 1; g >= 0; --g)
+        if (lg[i][g] >= 0) l = lg[i][g];
+      p0[i] = l;
+      r0[i] = l >= 0 ? min(a.lora_ranks[l], a.R) : 0;
+    }
+  }
 
   // Fragments are double-buffered in registers: the LDS reads of sub-step
   // ks+1 are issued before the MFMAs of sub-step ks.
@@ -577,79 +610,101 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] ------------------
   // Each 16-row group has its own slot; a BS-row block holds BS/16 groups, so
   // every distinct slot of the block gets its own pass with the rows of the
-  // other slots masked to zero.
+  // other slots masked to zero.  The first pass of every block (usually the
+  // only one) loads its first 16-deep rank step together with the other
+  // blocks', so the whole expand waits for memory about once.
   if (a.h != nullptr) {
-    constexpr int NG = BS / 16;
     constexpr int MAXKS = 64 / KF;   // RP <= 64
-    static_for<MB>([&](auto I) {
-      constexpr int i = decltype(I)::value;
+    // rank step ks of the pass serving slot l in block i: h of this lane's
+    // row (the block's first row, zeroed later, if its group is not served)
+    // and the B^T values of its column (rows q >= r never read: q clamped)
+    auto load_step = [&](int i, int l, int r, int ks, floatx8& hg, floatx8& hu, frag* bfv) {
       const int rb = wm * WM + i * BS;
-      if (rb >= nrows) return;
-      int lg[NG];
+      const int q0 = ks * KF + lk;
+      const bool mine = lg[i][lrow / 16] == l;
+      const float* hrow = a.h + (row0 + min(rb + (mine ? lrow : 0), nrows - 1)) * a.HS;
+      hg = *reinterpret_cast<const floatx8*>(hrow + q0);
+      hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int r16 = min(rb + 16 * g, nrows - 16);   // clamped: loads stay unconditional
-        const int l = a.tile_lora[(row0 + r16) / a.BM_tile];
-        const int lr = (l >= 0 && l < a.L) ? a.lora_ranks[l] : 0;
-        lg[g] = (rb + 16 * g < nrows && l >= 0 && l < a.L && lr > 0) ? l : -1;
+      for (int j = 0; j < NB; ++j) {
+        const bool up = GATE_UP && j >= NB / 2;
+        const T* pool = up ? a.b_pool1 : a.b_pool0;
+        const int64_t col = min(col_of(j) + lrow, a.n_out - 1);
+        const T* pb = pool + (((int64_t)max(l, 0) * a.E + e) * a.R) * a.n_out + col;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) bfv[j][v] = pb[(int64_t)min(q0 + v, max(r, 1) - 1) * a.n_out];
+      }
+    };
+    auto mma_step = [&](auto I, int l, int r, int ks, floatx8 hg, floatx8 hu, frag* bfv) {
+      constexpr int i = decltype(I)::value;
+      const int q0 = ks * KF + lk;
+      const bool mine = lg[i][lrow / 16] == l;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (!mine) { hg[v] = 0.0f; hu[v] = 0.0f; }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (q0 + v >= r || col_of(j) + lrow >= a.n_out) bfv[j][v] = E_::from_float(0.0f);
       }
 #pragma unroll
-      for (int pass = 0; pass < NG; ++pass) {
-        const int l = lg[pass];
-        if (l < 0) continue;
-        if (pass == 1 && lg[0] == l) continue;   // done together with group 0
-        const int r = min(a.lora_ranks[l], a.R);
-        const int nks = (r + KF - 1) / KF;
-        // rows of this lane's block row that belong to slot l; others read a
-        // valid row (the block's first) and are zeroed
-        const bool mine = lg[lrow / 16] == l;
-        const float* hrow = a.h + (row0 + rb + (mine ? lrow : 0)) * a.HS;
-        const T* pb[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const bool up = GATE_UP && j >= NB / 2;
-          const T* pool = up ? a.b_pool1 : a.b_pool0;
-          const int64_t col = min(col_of(j) + lrow, a.n_out - 1);
-          pb[j] = pool + (((int64_t)l * a.E + e) * a.R) * a.n_out + col;
-        }
-#pragma unroll
-        for (int ks = 0; ks < MAXKS; ++ks) {
-          if (ks >= nks) break;
-          const int q0 = ks * KF + lk;
-          floatx8 hg = *reinterpret_cast<const floatx8*>(hrow + q0);
-          floatx8 hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
-          // B^T rows q >= r are never read (q is clamped, the value zeroed)
-          frag bfv[NB];
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < 8; ++v) bfv[j][v] = pb[j][(int64_t)min(q0 + v, r - 1) * a.n_out];
+      for (int j = 0; j < NB; ++j) {
+        const bool up = GATE_UP && j >= NB / 2;
+        const floatx8& hv = up ? hu : hg;
+        if constexpr (sizeof(T) == 2) {
+          // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
+          frag hi, lo;
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            if (!mine) { hg[v] = 0.0f; hu[v] = 0.0f; }
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              if (q0 + v >= r || col_of(j) + lrow >= a.n_out) bfv[j][v] = E_::from_float(0.0f);
+            hi[v] = (bf16_t)hv[v];
+            lo[v] = (bf16_t)(hv[v] - (float)hi[v]);
           }
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const bool up = GATE_UP && j >= NB / 2;
-            const floatx8& hv = up ? hu : hg;
-            if constexpr (sizeof(T) == 2) {
-              // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
-              frag hi, lo;
-#pragma unroll
-              for (int v = 0; v < 8; ++v) {
-                hi[v] = (bf16_t)hv[v];
-                lo[v] = (bf16_t)(hv[v] - (float)hi[v]);
-              }
-              acc[i][j] = B_::mma(hi, bfv[j], acc[i][j]);
-              acc[i][j] = B_::mma(lo, bfv[j], acc[i][j]);
-            } else {
-              acc[i][j] = B_::mma(hv, bfv[j], acc[i][j]);
-            }
-          }
+          acc[i][j] = B_::mma(hi, bfv[j], acc[i][j]);
+          acc[i][j] = B_::mma(lo, bfv[j], acc[i][j]);
+        } else {
+          acc[i][j] = B_::mma(hv, bfv[j], acc[i][j]);
         }
+      }
+    };
+    // one pass: rank steps from ks0 on (ks0 = 1: step 0 already done)
+    auto pass_rest = [&](auto I, int l, int ks0) {
+      constexpr int i = decltype(I)::value;
+      const int r = min(a.lora_ranks[l], a.R);
+      const int nks = (r + KF - 1) / KF;
+#pragma unroll
+      for (int ks = 1; ks < MAXKS; ++ks) {
+        if (ks < ks0 || ks >= nks) continue;
+        floatx8 hg, hu;
+        frag bfv[NB];
+        load_step(i, l, r, ks, hg, hu, bfv);
+        mma_step(I, l, r, ks, hg, hu, bfv);
+      }
+    };
+    floatx8 hg0[MB], hu0[MB];
+    frag bf0[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) load_step(i, p0[i], r0[i], 0, hg0[i], hu0[i], bf0[i]);
+    static_for<MB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (p0[i] < 0) return;
+      mma_step(I, p0[i], r0[i], 0, hg0[i], hu0[i], bf0[i]);
+      pass_rest(I, p0[i], 1);
+    });
+    // further passes: groups whose slot differs from every earlier group's
+    static_for<MB>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+#pragma unroll
+      for (int g = 1; g < NG; ++g) {
+        const int l = lg[i][g];
+        bool seen = l < 0 || l == p0[i];
+#pragma unroll
+        for (int g2 = 0; g2 < g; ++g2) seen = seen || lg[i][g2] == l;
+        if (seen) continue;
+        const int r = min(a.lora_ranks[l], a.R);
+        floatx8 hg, hu;
+        frag bfv[NB];
+        load_step(i, l, r, 0, hg, hu, bfv);
+        mma_step(I, l, r, 0, hg, hu, bfv);
+        pass_rest(I, l, 1);
       }
     });
   }
@@ -718,10 +773,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     }
   }
   }();
-  __syncthreads();   // everyone has read the current claim
-  if (threadIdx.x == 0) claimed = next_claim;
-  __syncthreads();
-  logical = t_begin + claimed;
+  if (!published) {   // a skipped tile: publish here
+    __syncthreads();   // everyone has read the current claim
+    if (threadIdx.x == 0) claimed = next_claim;
+    __syncthreads();
+  }
+  logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);
   }  // persistent tile loop
 }
 
