@@ -11,5 +11,6 @@ from .moe_lora_oracle import (  # noqa: F401
     moe_lora_forward,
     moe_lora_forward_bruteforce,
     moe_lora_info,
+    moe_lora_route,
     silu,
 )

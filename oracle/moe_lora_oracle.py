@@ -293,3 +293,39 @@ def moe_lora_forward_bruteforce(x, topk_ids, topk_weights, w_gate_up, w_down,
             a = silu(gate) * up
             y[t] += w[t, j] * (Wd @ a)
     return y
+
+
+# ---------------------------------------------------------------------------
+# router (the layer configs: softmax over the experts, top-k, renormalised)
+# ---------------------------------------------------------------------------
+def moe_lora_route(logits, top_k: int):
+    """Return (topk_ids int32[T, k], topk_weights float64[T, k]).
+
+    Each token keeps the k experts of largest softmax probability, in
+    descending order with ties to the lower expert id, and their weights are
+    renormalised over the k.
+
+    Softmax is strictly increasing in the logit, so the ranking is the ranking
+    of the logits themselves, taken on the exact input values (fp64
+    probabilities of very negative logits can underflow to equal values and
+    would break ties differently).  In the renormalised weight the softmax
+    normaliser cancels: w_j = exp(l_j - m) / sum over the k of exp(l_i - m),
+    with m the largest logit.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    if lg.ndim != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = lg.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("need 1 <= top_k <= E")
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    expert = np.arange(E)
+    for t in range(T):
+        # primary key: descending logit; secondary: ascending expert id
+        order = np.lexsort((expert, -lg[t]))[:top_k]
+        ids[t] = order
+        top = lg[t, order]
+        e = np.exp(top - top[0])
+        w[t] = e / e.sum()
+    return ids, w

@@ -398,4 +398,65 @@ def pin_silu(orc):
     assert np.allclose(orc.silu(v), ref, rtol=1e-13, atol=1e-300)
 
 
+# ---------------------------------------------------------------------------
+# router: softmax over the experts -> top-k (ties to the lower id) -> renormalise
+# ---------------------------------------------------------------------------
+def _route_bruteforce(row, k):
+    """k rounds of: the largest remaining logit, the lowest id among equals;
+    weights in the ratio form w_j = 1 / sum_i exp(l_i - l_j) over the chosen."""
+    import math
+    left = list(range(len(row)))
+    ids = []
+    for _ in range(k):
+        best = left[0]
+        for e in left[1:]:
+            if row[e] > row[best]:
+                best = e
+        ids.append(best)
+        left.remove(best)
+    w = [1.0 / sum(math.exp(row[i] - row[j]) for i in ids) for j in ids]
+    return ids, w
+
+
+def pin_route_bruteforce(orc):
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        T, E = int(rng.integers(1, 6)), int(rng.integers(1, 11))
+        k = int(rng.integers(1, E + 1))
+        # few distinct values: many ties
+        lg = rng.integers(-3, 3, size=(T, E)).astype(np.float64) * (0.5 if trial % 2 else 1.0)
+        ids, w = orc.moe_lora_route(lg, k)
+        for t in range(T):
+            bi, bw = _route_bruteforce(list(lg[t]), k)
+            assert list(ids[t]) == bi, (lg[t], k, ids[t], bi)
+            assert np.allclose(w[t], bw, rtol=1e-12, atol=0), (w[t], bw)
+
+
+def pin_route_closed_forms(orc):
+    from scipy.special import softmax
+    rng = np.random.default_rng(32)
+    lg = rng.standard_normal((50, 12)) * 3
+    # k = E: the weights are the full softmax, in descending order
+    ids, w = orc.moe_lora_route(lg, 12)
+    p = softmax(lg, axis=1)
+    assert np.allclose(w, np.take_along_axis(p, ids.astype(np.int64), axis=1), rtol=1e-12)
+    assert np.all(np.diff(np.take_along_axis(lg, ids.astype(np.int64), axis=1), axis=1) <= 0)
+    # k = 1: the (first) argmax, weight 1
+    ids, w = orc.moe_lora_route(lg, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(lg, axis=1)) and np.all(w == 1.0)
+    # weights sum to one and their ratios are exp(l_i - l_j); shift invariance
+    ids, w = orc.moe_lora_route(lg, 4)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    sel = np.take_along_axis(lg, ids.astype(np.int64), axis=1)
+    assert np.allclose(w[:, 1] / w[:, 0], np.exp(sel[:, 1] - sel[:, 0]), rtol=1e-12)
+    ids2, w2 = orc.moe_lora_route(lg + 17.25, 4)
+    assert np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=1e-12)
+    # all logits equal: the k lowest ids, weight 1/k
+    ids, w = orc.moe_lora_route(np.zeros((3, 9)), 5)
+    assert np.array_equal(ids, np.tile(np.arange(5), (3, 1))) and np.allclose(w, 0.2)
+    # logits far below zero (probabilities that underflow in fp64): still ranked
+    ids, w = orc.moe_lora_route(np.array([[-2001.0, -2000.0, -2002.0]]), 2)
+    assert list(ids[0]) == [1, 0] and np.allclose(w[0], [1 / (1 + np.exp(-1.0)), 1 / (1 + np.exp(1.0))])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

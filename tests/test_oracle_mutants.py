@@ -30,6 +30,12 @@ MUTANTS = {
     "align_no_pad": ("ntiles = (n + BM - 1) // BM", "ntiles = max(1, n // BM)"),
     "undercover_never": ("if max_seg_len > 0 and bs * max_seg_len < num_tokens:", "if False:"),
     "brute_up_uses_gate": ("up = Wu @ X[t]", "up = Wg @ X[t]"),
+    "route_ties_to_higher_id": ("order = np.lexsort((expert, -lg[t]))[:top_k]",
+                                "order = np.lexsort((-expert, -lg[t]))[:top_k]"),
+    "route_ascending": ("order = np.lexsort((expert, -lg[t]))[:top_k]",
+                        "order = np.lexsort((expert, lg[t]))[:top_k]"),
+    "route_no_renorm": ("w[t] = e / e.sum()", "w[t] = e"),
+    "route_softmax_over_all": ("w[t] = e / e.sum()", "w[t] = e / np.exp(lg[t] - top[0]).sum()"),
     "brute_b_untransposed": ("Bd = _f64(b_down[l, e])[:r].T      # [H, r]", "Bd = _f64(b_down[l, e])[:r].T[::-1]"),
 }
 
