@@ -14,7 +14,8 @@
  * segments (SGLang PR #24160 page, "shared MoE LoRA batch info", sections
  * 实现拆解 and 关键源码片段).
  *
- * Three calls:
+ * Three calls, plus the router step before them:
+ *   moe_lora_route   -- per layer, optional: top-k experts and weights from router logits.
  *   moe_lora_info    -- once per batch: token_lora_mapping and adapter_enabled.
  *   moe_lora_align   -- per layer: bucket (token, expert) pairs by (expert, adapter),
  *                       padded to block_m rows.
@@ -54,6 +55,26 @@ typedef enum { MOE_LORA_F32 = 0, MOE_LORA_BF16 = 1 } moe_lora_dtype;
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_lora_status_str(int status);
+
+/*
+ * moe_lora_route -- the router step before the layer.  The pages' layer
+ * configurations define it as softmax over the experts, top-k, renormalised
+ * (the workload definitions of the MoE-LoRA pages); the order and the tie rule
+ * are this library's reading.
+ *
+ *   logits        [num_tokens, num_experts] fp32, row-major, finite values.
+ *   topk_ids      [num_tokens, top_k] out  int32: the top_k experts of largest
+ *                                 probability (equivalently logit), in descending
+ *                                 order, ties to the lower expert id.  Bit-exact.
+ *   topk_weights  [num_tokens, top_k] out  fp32: their softmax probabilities
+ *                                 renormalised over the top_k (sum to 1).
+ *
+ * 1 <= top_k <= num_experts, top_k <= 16 (else MOE_LORA_ERR_UNSUPPORTED).
+ * num_tokens == 0 enqueues nothing.  The outputs feed moe_lora_align and
+ * moe_lora_forward directly.
+ */
+int moe_lora_route(int32_t num_tokens, int32_t num_experts, int32_t top_k, const float* logits,
+                   int32_t* topk_ids, float* topk_weights, void* stream);
 
 /*
  * moe_lora_info -- per-batch MoE-LoRA metadata (SGLang PR #24160 page,

@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     moe_lora_forward,
     moe_lora_forward_workspace_bytes,
     moe_lora_info,
+    moe_lora_route,
     run_layer,
 )

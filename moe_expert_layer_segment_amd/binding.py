@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     L.moe_lora_status_str.restype = ctypes.c_char_p
     L.moe_lora_status_str.argtypes = [ctypes.c_int]
+    L.moe_lora_route.restype = ctypes.c_int
+    L.moe_lora_route.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4
     L.moe_lora_info.restype = ctypes.c_int
     L.moe_lora_info.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 6
     L.moe_lora_align_capacity_rows.restype = ctypes.c_int64
@@ -114,6 +116,27 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, numel=None):
         raise ValueError(f"{name} must be on {device}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+def moe_lora_route(logits: torch.Tensor, top_k: int, topk_ids: Optional[torch.Tensor] = None,
+                   topk_weights: Optional[torch.Tensor] = None):
+    """(topk_ids int32 [T, k], topk_weights fp32 [T, k]) from fp32 router logits [T, E]."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _need(topk_ids, "topk_ids", torch.int32, logits.device, T * top_k)
+    _need(topk_weights, "topk_weights", torch.float32, logits.device, T * top_k)
+    _check(lib().moe_lora_route(T, E, top_k, _ptr(logits), _ptr(topk_ids), _ptr(topk_weights),
+                                _stream()), "moe_lora_route")
+    return topk_ids, topk_weights
 
 
 # ---------------------------------------------------------------------------

@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_lora.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "info.hip", "align.hip", "forward.hip"]
+SOURCES = ["api.cpp", "route.hip", "info.hip", "align.hip", "forward.hip"]
 ARCH = "gfx950"
 
 

@@ -33,6 +33,16 @@ const char* moe_lora_status_str(int status) {
   }
 }
 
+int moe_lora_route(int32_t num_tokens, int32_t num_experts, int32_t top_k, const float* logits,
+                   int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (num_tokens < 0 || num_experts <= 0 || top_k <= 0 || top_k > num_experts)
+    return MOE_LORA_ERR_INVALID;
+  if (top_k > route_max_k()) return MOE_LORA_ERR_UNSUPPORTED;
+  if (num_tokens > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_LORA_ERR_INVALID;
+  return hip_status(launch_route(num_tokens, num_experts, top_k, logits, topk_ids, topk_weights,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 int moe_lora_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras, int32_t max_seg_len,
                   const int32_t* seg_indptr, const int32_t* weight_indices,
                   const int32_t* lora_ranks, int32_t* adapter_enabled,

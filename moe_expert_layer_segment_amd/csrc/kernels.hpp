@@ -29,6 +29,10 @@ hipError_t launch_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
                        const int32_t* lora_ranks, int32_t* adapter_enabled,
                        int32_t* token_lora_mapping, hipStream_t stream);
 
+int route_max_k();
+hipError_t launch_route(int32_t T, int32_t E, int32_t k, const float* logits, int32_t* topk_ids,
+                        float* topk_weights, hipStream_t stream);
+
 hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
                         const int32_t* topk_ids, const int32_t* mapping, const int32_t* enabled,
                         int32_t* sorted_ids, int32_t* tile_expert, int32_t* tile_lora,

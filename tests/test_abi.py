@@ -87,6 +87,20 @@ def test_info_validation_codes():
     assert f(0, 0, 0, 0, FAKE, None, None, None, None, None) == binding.OK
 
 
+def test_route_validation_codes():
+    lib = binding.lib()
+    f = lib.moe_lora_route
+    assert f(-1, 8, 2, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 0, 1, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 8, 0, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 8, 9, FAKE, FAKE, FAKE, None) == binding.ERR_INVALID       # top_k > E
+    assert f(4, 64, 17, FAKE, FAKE, FAKE, None) == binding.ERR_UNSUPPORTED  # top_k > 16
+    assert f(4, 8, 2, None, FAKE, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 8, 2, FAKE, None, FAKE, None) == binding.ERR_INVALID
+    assert f(4, 8, 2, FAKE, FAKE, None, None) == binding.ERR_INVALID
+    assert f(0, 8, 2, None, None, None, None) == binding.OK                 # nothing enqueued
+
+
 def test_align_validation_codes():
     lib = binding.lib()
     f = lib.moe_lora_align

@@ -1,0 +1,67 @@
+"""GPU router (softmax -> top-k, ties to the lower id -> renormalised) against
+the oracle: expert ids bit-exact, weights within fp32 rounding, on the router
+logits of every workload, planted ties, the k = 1 / k = E / large-E edges, and
+the whole layer run from logits."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_layer_close, gpu_inputs, oracle_forward, run, say, to_np
+from moe_expert_layer_segment_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+
+W_RTOL = 2e-6   # fp32 exp / divide against the fp64 oracle
+
+
+def _check(logits32: np.ndarray, k: int, what: str):
+    ids, w = binding.moe_lora_route(torch.from_numpy(logits32).cuda(), k)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.moe_lora_route(logits32.astype(np.float64), k)
+    got_ids = ids.cpu().numpy()
+    bad = np.nonzero((got_ids != ref_ids).any(axis=1))[0]
+    assert bad.size == 0, (what, bad[:5], got_ids[bad[:5]], ref_ids[bad[:5]])
+    got_w = w.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(got_w - ref_w) / np.maximum(np.abs(ref_w), 1e-30)) if ref_w.size else 0.0
+    say(f"  route {what}: T={logits32.shape[0]} E={logits32.shape[1]} k={k} max rel w err {err:.2e}")
+    assert err <= W_RTOL, (what, err)
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_route_workload_logits(name):
+    spec = workloads.config(name)
+    lg = workloads.router_logits(spec).astype(np.float32)
+    _check(lg, spec.top_k, name)
+
+
+def test_route_ties_and_edges():
+    rng = np.random.default_rng(41)
+    # few distinct values: ties everywhere
+    _check(rng.integers(-2, 3, size=(1000, 16)).astype(np.float32), 4, "ties")
+    _check(np.zeros((10, 7), np.float32), 3, "all equal")
+    lg = rng.standard_normal((777, 33)).astype(np.float32)
+    _check(lg, 1, "k=1")
+    _check(lg[:, :16], 16, "k=E=16")
+    _check(rng.standard_normal((300, 1024)).astype(np.float32) * 4, 16, "E=1024 k=16")
+    _check((rng.standard_normal((64, 12)) - 3000).astype(np.float32), 3, "very negative logits")
+    _check(np.zeros((0, 8), np.float32), 2, "empty")
+
+
+def test_layer_from_logits():
+    """router -> info -> align -> forward on the GPU equals oracle router -> oracle layer."""
+    spec = workloads.LayerSpec("from_logits", 8, 2, 256, 256, 3, [16, 8, 0], [40, 25, 31],
+                               [0, 1, 2], seed=42, pool_rank=16)
+    say("layer from router logits")
+    inp = gpu_inputs(spec)
+    lg = workloads.router_logits(spec).astype(np.float32)
+    ids, w = binding.moe_lora_route(torch.from_numpy(lg).cuda(), spec.top_k)
+    ref_ids, ref_w = oracle.moe_lora_route(lg.astype(np.float64), spec.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    inp = dict(inp)
+    inp["topk_ids"], inp["topk_weights"] = ids, w
+    # the oracle layer runs on the oracle router's output (fp32-rounded weights,
+    # as the layer takes fp32 router weights)
+    inp["meta"] = dict(inp["meta"], topk_ids=ref_ids, topk_weights=ref_w.astype(np.float32))
+    got = to_np(run(inp, out_dtype=torch.float32))
+    assert_layer_close(got, oracle_forward(inp), "bf16", "layer from logits")
