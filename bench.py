@@ -334,6 +334,21 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
+    # the router step before the layer (not part of the step): its time on this
+    # workload's router logits, events on the current stream (the launch stream)
+    logits = torch.from_numpy(workloads.router_logits(spec).astype(np.float32)).to(dev)
+    r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        binding.moe_lora_route(logits, k, r_ids, r_w)
+    r_start, r_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r_start.record()
+    for _ in range(20):
+        binding.moe_lora_route(logits, k, r_ids, r_w)
+    r_stop.record()
+    torch.cuda.synchronize()
+    router_ms = r_start.elapsed_time(r_stop) / 20
+
     c = counts(spec, inp["meta"])
     gu_ms = stage_ms["gate_up_gemm"]
     achieved = c["gate_up_flops"] / (gu_ms * 1e-3) / 1e12
@@ -380,6 +395,7 @@ def main():
                   "algorithmic_flops": c["total_flops"], "algorithmic_bytes": c["total_bytes"],
                   "active_experts": c["active_experts"], "lora_buckets": c["lora_buckets"]},
         "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "router_ms": round(router_ms, 4),
     }
     print(json.dumps(out), flush=True)
 
