@@ -141,10 +141,26 @@ def config(name: str) -> LayerSpec:
         return LayerSpec(f"{name}_large_expert_{'prefill' if name == 'c4p' else 'decode'}",
                          256, 8, 7168, 2048, 8, [32] * 8, lens, wi, seed=4,
                          router="uniform_bias", pool_rank=32)
+    if name == "c1_tp8":
+        # one rank of c1 under 8-way tensor parallelism: I split 8 ways
+        c1 = config("c1")
+        return LayerSpec("c1_tp8_rank", c1.num_experts, c1.top_k, c1.hidden, c1.inter // 8,
+                         c1.num_loras, c1.lora_ranks, c1.seg_lens, c1.weight_indices,
+                         seed=c1.seed, router=c1.router, pool_rank=c1.pool_rank)
+    if name in ("c4p_ep8", "c4d_ep8"):
+        # one rank of c4 under 8-way expert parallelism: 32 local experts; each
+        # dispatched (token, expert) pair arrives as a row routed to one expert
+        # (k = 8 pairs per token, 1/8 of them local: about one row per token)
+        c4 = config(name[:3])
+        lens, wi = c4.seg_lens, c4.weight_indices
+        return LayerSpec(f"{name}_rank", 32, 1, c4.hidden, c4.inter, c4.num_loras, c4.lora_ranks,
+                         lens, wi, seed=c4.seed, router="uniform_bias", pool_rank=c4.pool_rank)
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("c0", "c1", "c2", "c3", "c4p", "c4d")
+# one rank's share of a layer under tensor / expert parallelism (shapes only)
+SHARD_CONFIG_NAMES = ("c1_tp8", "c4p_ep8", "c4d_ep8")
 
 
 # ----------------------------------------------------------------------------
