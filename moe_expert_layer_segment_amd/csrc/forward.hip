@@ -193,6 +193,201 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
     }
 }
 
+// The same shrink with the pool rows shared through LDS: a workgroup takes
+// 4 consecutive 16-row groups (one per wave) of one K split; when they belong
+// to one (expert, slot) bucket -- the common case -- the bucket's pool rows
+// are loaded once per 128-deep K chunk into LDS by the whole workgroup
+// (double-buffered, register-staged) and each wave multiplies its own rows
+// against them.  A wave whose group has another slot reads its pool rows from
+// global memory instead.  Pool rows past the slot's rank are never read.
+template <typename T, int NPOOL>
+__global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
+  typedef Elt<T> E_;
+  typedef typename E_::frag frag;
+  constexpr int NQB = 4;                            // up to 64 rank columns per pool
+  constexpr int KC = 256 / (int)sizeof(T);          // K elements per LDS chunk (256 B a row)
+  constexpr int CPQ = KC * (int)sizeof(T) / 16;     // 16-byte chunks per pool row and chunk
+  constexpr int ROWEL = KC;                         // elements per LDS pool row
+  // two buffers of NPOOL * RP rows of ROWEL elements (dynamic LDS, sized by the launch)
+  extern __shared__ __attribute__((aligned(16))) unsigned char shrink4_lds[];
+  T* const pool_lds = reinterpret_cast<T*>(shrink4_lds);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t nrp = a.num_rows_padded[0];
+  const int64_t g0 = (int64_t)blockIdx.x * 4;       // the workgroup's first group
+  if (g0 * 16 >= nrp) return;
+  const int64_t k_begin = (int64_t)blockIdx.y * a.kchunk;
+  const int64_t k_end = min(a.K, k_begin + a.kchunk);
+  const int HS = NPOOL * a.RP;
+
+  // slot, expert and rank of group g0 + w; false when the group has no rows
+  // or no slot (its h rows are not written, as in shrink_kernel)
+  auto group_key = [&](int w, int& l, int& e, int& r) -> bool {
+    const int64_t row0 = (g0 + w) * 16;
+    l = -1; e = -1; r = 0;
+    if (row0 >= nrp || row0 + 16 > a.cap) return false;
+    const int tile = (int)(row0 / a.BM);
+    l = a.tile_lora[tile];
+    e = a.tile_expert[tile];
+    if (l < 0 || l >= a.L || e < 0 || e >= a.E) return false;
+    r = min(a.lora_ranks[l], a.R);
+    return true;
+  };
+  // the shared bucket: the first group's with a positive rank
+  int sl = -1, se = -1, sr = 0;
+  for (int w = 0; w < 4; ++w) {
+    int l, e, r;
+    if (group_key(w, l, e, r) && r > 0) { sl = l; se = e; sr = r; break; }
+  }
+  int l, e, r;
+  const bool live = group_key(wave, l, e, r);
+  const int64_t row0 = (g0 + wave) * 16;
+  if (live && r <= 0) {
+    // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
+    float* hz = a.h + (int64_t)blockIdx.y * a.split_stride + row0 * HS;
+    for (int i = lane; i < 16 * HS; i += 64) hz[i] = 0.0f;
+  }
+  if (sl < 0) return;                               // no positive rank in these groups (uniform)
+  const bool active = live && r > 0;
+  const bool shared = active && l == sl && e == se;
+
+  const int my_row = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const T* arow = nullptr;
+  if (active) {
+    const int64_t row = row0 + my_row;
+    if (a.gathered) {
+      const int pid = a.sorted_ids[row];
+      if (pid < a.P) arow = a.src + (int64_t)(pid / a.top_k) * a.K;
+    } else {
+      arow = a.src + row * a.K;
+    }
+  }
+  // this wave's own pool rows (used when its slot is not the shared one)
+  const T* prow[NPOOL][NQB];
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi) {
+    const T* pool = pi == 0 ? a.pool0 : a.pool1;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int q = qb * 16 + my_row;
+      prow[pi][qb] = (active && q < r) ? pool + (((int64_t)l * a.E + e) * a.R + q) * a.K : nullptr;
+    }
+  }
+  const int nqb = (r + 15) / 16;
+  floatx4 acc[NPOOL][NQB];
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) acc[pi][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // cooperative load of the shared pool rows q < sr of one K chunk: 16-byte
+  // pieces, LDS row q of pool pi with piece c stored at piece c ^ (q % CPQ)
+  // (16 consecutive rows read at one piece hit distinct banks)
+  const int RPL = a.RP;                             // LDS rows per pool
+  const int64_t buf_elems = (int64_t)NPOOL * RPL * ROWEL;
+  const int PIECES = NPOOL * RPL * CPQ;
+  constexpr int PER_THREAD = (NPOOL * 64 * CPQ + 255) / 256;  // RP <= 64
+  int4v stage[PER_THREAD];
+  auto load_chunk = [&](int64_t kc0, int valid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = threadIdx.x + i * 256;
+      const int pi = c / (RPL * CPQ), q = (c / CPQ) % RPL, pc = c % CPQ;
+      const bool ok = c < PIECES && q < sr && pc * (16 / (int)sizeof(T)) < valid;
+      const T* pool = pi == 0 ? a.pool0 : a.pool1;
+      stage[i] = ok ? *reinterpret_cast<const int4v*>(
+                          pool + (((int64_t)sl * a.E + se) * a.R + q) * a.K + kc0 + pc * (16 / (int)sizeof(T)))
+                    : int4v{0, 0, 0, 0};
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c >= PIECES) continue;
+      const int pi = c / (RPL * CPQ), q = (c / CPQ) % RPL, pc = c % CPQ;
+      *reinterpret_cast<int4v*>(&pool_lds[buf * buf_elems + (pi * RPL + q) * ROWEL +
+                                          ((pc ^ (q % CPQ)) * 16 / (int)sizeof(T))]) = stage[i];
+    }
+  };
+  // one frag (8 K elements from kel) of LDS pool row q
+  auto lds_frag = [&](int buf, int pi, int q, int kel) -> frag {
+    constexpr int EPP = 16 / (int)sizeof(T);       // elements per piece
+    frag f;
+    if constexpr (sizeof(T) == 2) {
+      const int pc = kel / EPP;
+      f = *reinterpret_cast<const frag*>(&pool_lds[buf * buf_elems + (pi * RPL + q) * ROWEL + ((pc ^ (q % CPQ)) * EPP)]);
+    } else {
+      const int pc = kel / EPP;
+      const T* rowp = &pool_lds[buf * buf_elems + (pi * RPL + q) * ROWEL];
+      const floatx4 lo = *reinterpret_cast<const floatx4*>(rowp + ((pc ^ (q % CPQ)) * EPP));
+      const floatx4 hi = *reinterpret_cast<const floatx4*>(rowp + (((pc + 1) ^ (q % CPQ)) * EPP));
+      f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+      f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    }
+    return f;
+  };
+
+  const int nchunks = (int)ceil_div(k_end - k_begin, KC);
+  if (nchunks > 0) {
+    load_chunk(k_begin, (int)min<int64_t>(KC, k_end - k_begin));
+    store_chunk(0);
+  }
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t kc0 = k_begin + (int64_t)c * KC;
+    const int valid = (int)min<int64_t>(KC, k_end - kc0);
+    __syncthreads();   // chunk c is in LDS; everyone is done with chunk c-1
+    const bool more = c + 1 < nchunks;
+    // this chunk's A rows are requested before the next pool chunk, so that
+    // waiting for them does not wait for the prefetch
+    frag avs[KC / 32];
+#pragma unroll
+    for (int j = 0; j < KC / 32; ++j)
+      avs[j] = (active && arow && j * 32 < valid) ? load_frag_global<T>(arow + kc0 + j * 32 + kq) : E_::zero();
+    if (more) load_chunk(kc0 + KC, (int)min<int64_t>(KC, k_end - kc0 - KC));
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < KC / 32; ++j) {
+        if (j * 32 >= valid) break;
+        const int ks = j * 32;
+        const frag av = avs[j];
+#pragma unroll
+        for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            if (qb >= nqb) continue;
+            const int q = qb * 16 + my_row;
+            frag bv;
+            if (shared)
+              bv = q < r ? lds_frag(c & 1, pi, q, ks + kq) : E_::zero();
+            else
+              bv = prow[pi][qb] ? load_frag_global<T>(prow[pi][qb] + kc0 + ks + kq) : E_::zero();
+            acc[pi][qb] = E_::mma(av, bv, acc[pi][qb]);
+          }
+      }
+    }
+    if (more) store_chunk((c + 1) & 1);
+  }
+  if (!active) return;
+  const float sc = a.scaling[l];
+  float* hrow_base = a.h + (int64_t)blockIdx.y * a.split_stride + row0 * HS;
+  // C layout: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 block
+#pragma unroll
+  for (int pi = 0; pi < NPOOL; ++pi)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int col = qb * 16 + (lane & 15);
+      if (col >= a.RP) continue;
+      const floatx4 t = acc[pi][qb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = (lane >> 4) * 4 + i;
+        const float v = (qb < nqb && col < r) ? sc * t[i] : 0.0f;
+        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
+      }
+    }
+}
+
 // h[0] += h[1] + ... + h[S-1] over the padded rows, in split order
 __global__ void __launch_bounds__(256)
 shrink_reduce_kernel(float* __restrict__ h, int64_t split_stride, int splits,
@@ -851,13 +1046,44 @@ static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : 
 // K splits of a shrink: enough workgroups to fill the GPU when the batch has
 // few rows (decode), each split at least 512 deep and a multiple of 128 (the
 // four waves' interleaved 32-deep steps).
-static int64_t shrink_kchunk(int64_t P, int64_t K) {
+// The shrink shares pool rows across 4 row groups on large batches whose
+// (expert, slot) buckets hold at least 64 pairs on average (4 groups of 16
+// rows).  Smaller buckets leave little to share; on smaller batches the
+// narrower grid and its per-chunk barriers cost more than the pool re-reads.
+#ifndef MOELORA_SHRINK4_MIN_ROWS
+#define MOELORA_SHRINK4_MIN_ROWS 64
+#endif
+#ifndef MOELORA_SHRINK4_MIN_P
+#define MOELORA_SHRINK4_MIN_P 65536
+#endif
+
+static bool use_shrink4(int64_t P, int64_t E, int64_t L) {
+  return L > 0 && P >= (int64_t)MOELORA_SHRINK4_MIN_P && P >= (int64_t)MOELORA_SHRINK4_MIN_ROWS * E * L;
+}
+
+template <typename T, int NPOOL>
+static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bool shared,
+                          hipStream_t stream) {
+  if (shared)  // two LDS buffers of NPOOL * RP pool rows of 256 bytes
+    hipLaunchKernelGGL((shrink4_kernel<T, NPOOL>), dim3((unsigned)ceil_div(groups, 4), (unsigned)splits),
+                       dim3(256), (size_t)2 * NPOOL * s.RP * 256, stream, s);
+  else
+    hipLaunchKernelGGL((shrink_kernel<T, NPOOL>), dim3((unsigned)groups, (unsigned)splits),
+                       dim3(256), 0, stream, s);
+}
+
+// K elements per split: enough splits for about 1024 workgroups of 4 waves,
+// each split at least 512 deep
+static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared) {
   const int64_t groups = P / 16 + 1;
-  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(1024, groups)));
+  const int64_t wgs = shared ? ceil_div(groups, 4) : groups;
+  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(1024, wgs)));
   s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
   return round_up(ceil_div(K, s), 128);
 }
-static int shrink_splits(int64_t P, int64_t K) { return (int)ceil_div(K, shrink_kchunk(P, K)); }
+static int shrink_splits(int64_t P, int64_t K, bool shared) {
+  return (int)ceil_div(K, shrink_kchunk(P, K, shared));
+}
 
 ForwardWs forward_ws_layout(const ForwardProblem& p) {
   ForwardWs w;
@@ -872,8 +1098,9 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
   w.count_off = take(sizeof(int32_t) * 20);   // item count, then 2 x 8 tile counters
-  w.split_gu = shrink_splits(p.T * p.k, p.H);
-  w.split_d = shrink_splits(p.T * p.k, p.I);
+  w.shrink4 = use_shrink4(P, p.E, p.L);
+  w.split_gu = shrink_splits(P, p.H, w.shrink4);
+  w.split_d = shrink_splits(P, p.I, w.shrink4);
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
@@ -926,10 +1153,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hgu;
     s.cap = w.cap;
-    s.kchunk = shrink_kchunk(P, p.H);
+    s.kchunk = shrink_kchunk(P, p.H, w.shrink4);
     s.split_stride = w.cap * 2 * w.RP;
-    hipLaunchKernelGGL((shrink_kernel<T, 2>), dim3((unsigned)groups, (unsigned)w.split_gu),
-                       dim3(256), 0, stream, s);
+    launch_shrink<T, 2>(s, groups, w.split_gu, w.shrink4, stream);
     if (w.split_gu > 1)
       hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * 2 * w.RP / 4, 256)),
                          dim3(256), 0, stream, hgu, (int64_t)s.split_stride, w.split_gu,
@@ -992,10 +1218,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hd;
     s.cap = w.cap;
-    s.kchunk = shrink_kchunk(P, p.I);
+    s.kchunk = shrink_kchunk(P, p.I, w.shrink4);
     s.split_stride = w.cap * w.RP;
-    hipLaunchKernelGGL((shrink_kernel<T, 1>), dim3((unsigned)groups, (unsigned)w.split_d),
-                       dim3(256), 0, stream, s);
+    launch_shrink<T, 1>(s, groups, w.split_d, w.shrink4, stream);
     if (w.split_d > 1)
       hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.RP / 4, 256)),
                          dim3(256), 0, stream, hd, (int64_t)s.split_stride, w.split_d,

@@ -1,7 +1,8 @@
 """GPU parity of the layer on the degenerate and extreme cases of the method:
 an empty batch, requests of length zero, every pair routed to one expert,
-every token routed to every expert, and the largest expert x slot key space
-the align step supports (E * (L + 1) = 32768)."""
+every token routed to every expert, the largest expert x slot key space
+the align step supports (E * (L + 1) = 32768), and a batch large enough for
+the shrinks to share pool rows across row groups."""
 import numpy as np
 import pytest
 import torch
@@ -89,3 +90,21 @@ def test_largest_expert_slot_key_space():
     say("forward edge: E * (L + 1) = 32768")
     inp = gpu_inputs(spec)
     assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", "E*(L+1)=32768")
+
+
+@pytest.mark.parametrize("dtype,block_m", [("bf16", 16), ("bf16", 128), ("f32", 16)])
+def test_large_batch_shared_pool_shrink(dtype, block_m):
+    # over 64K pairs with large (expert, slot) buckets: the shrinks share each
+    # bucket's pool rows across 4 row groups; with 16-row tiles many 4-group
+    # spans straddle two buckets (the groups of the other bucket read their pool
+    # rows directly), and slot 1 has rank 0
+    rng = np.random.default_rng(26)
+    segs = [int(v) for v in rng.integers(200, 1600, size=48)]
+    wi = [int(v) for v in rng.integers(-1, 3, size=48)]
+    spec = workloads.LayerSpec("shared_shrink", 4, 2, 128, 192, 3, [16, 0, 12], segs, wi,
+                               dtype=dtype, seed=26, pool_rank=16)
+    assert spec.num_tokens * spec.top_k >= 65536
+    say(f"forward edge: shared-pool shrink, {spec.num_tokens} tokens, {dtype}, block_m={block_m}")
+    inp = gpu_inputs(spec)
+    assert_layer_close(_y32(inp, block_m=block_m), oracle_forward(inp), dtype,
+                       f"shared-pool shrink {dtype} bm={block_m}")
