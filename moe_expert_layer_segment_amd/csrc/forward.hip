@@ -430,7 +430,8 @@ template <typename T>
 struct GemmArgs {
   const int4* items;
   const int32_t* item_count;
-  int max_items, n_tiles;
+  int max_items, n_tiles;      // n_tiles: column tiles x K splits
+  int n_cols, ksplit;           // column tiles; K splits (down only, else 1)
   // A operand
   const T* a_src;             // x [T, K] (gate_up, gathered) or act [cap, K] (down)
   const int32_t* sorted_ids;
@@ -451,7 +452,7 @@ struct GemmArgs {
   const T* b_pool1;           // [L, E, R, n_out] (up) or null
   // outputs
   T* act;                     // gate_up: [cap, n_out]
-  float* z;                   // down: [P, n_out]
+  float* z;                   // down: [ksplit, P, n_out], one plane per K split
   const float* topk_weights;
   int64_t cap;                // rows of sorted_ids / act / h
   int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
@@ -568,8 +569,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   const int g_n = gbase + (gj < grem ? 1 : 0);
   const int local = logical - (first + g_off) * a.n_tiles;
   const int item_idx = first + g_off + local % g_n;
-  const int ntile = local / g_n;
-  if (item_idx >= count || ntile >= a.n_tiles) return;
+  const int col_t = local / g_n;                 // column tile x K split
+  if (item_idx >= count || col_t >= a.n_tiles) return;
+  const int split = col_t / a.n_cols;            // K split (split-major: a window shares its x rows)
+  const int ntile = col_t - split * a.n_cols;
+  const int64_t kper = a.K / a.ksplit;           // K elements per split, a multiple of BK
+  const bool lora_here = a.h != nullptr && split == 0;   // the expand is added once
   const int4 item = a.items[item_idx];
   const int64_t row0 = item.x;
   const int nrows = item.y;
@@ -653,7 +658,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // this wave's DMA instructions [I0, I1) of one stage
   auto issue_part = [&](auto i0_c, auto i1_c, int stage_k, int buf) {
     constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
-    const uint32_t kbytes = (uint32_t)stage_k * ROWB;
+    const uint32_t kbytes = (uint32_t)((int64_t)split * (kper / BK) + stage_k) * ROWB;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const int seg = wave * SEG_PER_WAVE + i;
@@ -661,7 +666,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       dma16(base, src_off[i] + kbytes, lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
   };
-  const int nk = (int)(a.K / BK);
+  const int nk = (int)(kper / BK);
   auto issue_stage = [&](int stage_k, int buf) {
     issue_part(std::integral_constant<int, 0>{}, std::integral_constant<int, SEG_PER_WAVE>{},
                stage_k, buf);
@@ -709,7 +714,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // block's first pass (its first served group), r0[i] its rank.
   constexpr int NG = BS / 16;
   int lg[MB][NG], p0[MB], r0[MB];
-  if (a.h != nullptr) {
+  if (lora_here) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int rb = wm * WM + i * BS;
@@ -808,7 +813,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // other slots masked to zero.  The first pass of every block (usually the
   // only one) loads its first 16-deep rank step together with the other
   // blocks', so the whole expand waits for memory about once.
-  if (a.h != nullptr) {
+  if (lora_here) {
     constexpr int MAXKS = 64 / KF;   // RP <= 64
     // rank step ks of the pass serving slot l in block i: h of this lane's
     // row (the block's first row, zeroed later, if its group is not served)
@@ -964,7 +969,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       floatx4 vv = *reinterpret_cast<const floatx4*>(ep + r * WN + cc * CH);
 #pragma unroll
       for (int q = 0; q < 4; ++q) vv[q] = wgt * vv[q];
-      *reinterpret_cast<floatx4*>(a.z + (int64_t)pid * a.n_out + col) = vv;
+      *reinterpret_cast<floatx4*>(a.z + ((int64_t)split * a.P + pid) * a.n_out + col) = vv;
     }
   }
   }();
@@ -978,19 +983,22 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 }
 
 // --------------------------------------------------------------------------
-// combine: y[t, c] = sum_j z[t*k + j, c]  (j in order, fp32)
+// combine: y[t, c] = sum_j sum_q z[q, t*k + j, c]  (j, then the down GEMM's
+// K splits q, in order, fp32)
 // --------------------------------------------------------------------------
 template <typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H) {
+combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H,
+               int nsplit, int64_t split_stride) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T_ * H) return;
   const int64_t t = i / H, c = i % H;
   floatx4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    floatx4 v = *reinterpret_cast<const floatx4*>(z + (t * k + j) * H + c);
-    s += v;
-  }
+  for (int j = 0; j < k; ++j)
+    for (int q = 0; q < nsplit; ++q) {   // pair j's K splits, in order
+      floatx4 v = *reinterpret_cast<const floatx4*>(z + q * split_stride + (t * k + j) * H + c);
+      s += v;
+    }
 #pragma unroll
   for (int q = 0; q < 4; ++q) y[i + q] = Elt<OutT>::from_float(s[q]);
 }
@@ -1039,6 +1047,22 @@ template <> struct TileCfg<float> {
 static int64_t gemm_grid(int64_t tiles, int per_cu) {
   const int64_t full = 256 * per_cu;
   return tiles >= full ? full : round_up(tiles > 0 ? tiles : 1, 8);
+}
+
+// K splits of the down GEMM.  With few, long tiles (a long I and fewer than 8
+// tiles per workgroup) the last round of the persistent grid leaves part of
+// the GPU idle for a whole tile; two K halves double the tile count and halve
+// that loss.  The tile count is estimated from P, E and the tile shape only
+// (one item per BM pairs plus a partial one per expert), so the choice, and
+// with it the rounding of y, does not depend on the align block size.
+template <typename T>
+static int down_ksplit(int64_t P, int64_t E, int64_t H, int64_t I) {
+  constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN_DOWN, BK = TileCfg<T>::ROWB / (int)sizeof(T);
+  const int64_t items = ceil_div(P, BM) + std::min(P, E);
+  const int64_t tiles = items * ceil_div(H, BN);
+  const int64_t slots = 256 * (int64_t)TileCfg<T>::PER_CU;
+  if (P <= 0 || I % (2 * BK) != 0 || I / 2 < 4096 || tiles >= 8 * slots) return 1;
+  return 2;
 }
 
 static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : TileCfg<float>::BM; }
@@ -1104,7 +1128,8 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
-  w.z_off = take(sizeof(float) * (size_t)P * p.H);
+  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I) : down_ksplit<float>(P, p.E, p.H, p.I);
+  w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
   w.bytes = off;
   return w;
 }
@@ -1186,7 +1211,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.w = static_cast<const T*>(p.w_gate_up);
     a.n_out = p.I;
     a.w_rows = 2 * p.I;
-    a.n_tiles = (int)ceil_div(p.I, BN / 2);
+    a.n_cols = (int)ceil_div(p.I, BN / 2);
+    a.ksplit = 1;
+    a.n_tiles = a.n_cols;
     a.h = lora ? hgu : nullptr;
     a.HS = 2 * (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b_gate);
@@ -1236,7 +1263,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.n_out = p.H;
     a.w_rows = p.H;
     constexpr int BND = TileCfg<T>::BN_DOWN, SD = TileCfg<T>::STAGES_DOWN;
-    a.n_tiles = (int)ceil_div(p.H, BND);
+    a.n_cols = (int)ceil_div(p.H, BND);
+    a.ksplit = w.split_down_k;
+    a.n_tiles = a.n_cols * a.ksplit;
     a.h = lora ? hd : nullptr;
     a.HS = (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b_down);
@@ -1254,10 +1283,10 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     const int64_t n4 = p.T * p.H / 4;
     if (p.out_f32)
       hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<float*>(p.y), p.T, (int)p.k, p.H);
+                         stream, z, static_cast<float*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
     else
       hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<T*>(p.y), p.T, (int)p.k, p.H);
+                         stream, z, static_cast<T*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
   }
   mark(2 * kStageCombine + 1);
   return hipGetLastError();

@@ -59,6 +59,7 @@ struct ForwardWs {
   size_t items_off, count_off, hgu_off, act_off, hd_off, z_off, bytes;
   int split_gu = 1, split_d = 1;   // K splits of the two shrinks
   bool shrink4 = false;            // shrinks share pool rows across 4 row groups
+  int split_down_k = 1;            // K splits of the down GEMM (planes of z)
 };
 ForwardWs forward_ws_layout(const ForwardProblem& p);
 // stages of the forward, in launch order (index into the optional event pairs)

@@ -1,8 +1,9 @@
 """GPU parity of the layer on the degenerate and extreme cases of the method:
 an empty batch, requests of length zero, every pair routed to one expert,
 every token routed to every expert, the largest expert x slot key space
-the align step supports (E * (L + 1) = 32768), and a batch large enough for
-the shrinks to share pool rows across row groups."""
+the align step supports (E * (L + 1) = 32768), a batch large enough for the
+shrinks to share pool rows across row groups, and an intermediate size long
+enough for the down GEMM to split K."""
 import numpy as np
 import pytest
 import torch
@@ -108,3 +109,15 @@ def test_large_batch_shared_pool_shrink(dtype, block_m):
     inp = gpu_inputs(spec)
     assert_layer_close(_y32(inp, block_m=block_m), oracle_forward(inp), dtype,
                        f"shared-pool shrink {dtype} bm={block_m}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_down_gemm_k_split(dtype):
+    # a long intermediate size and few tiles: the down GEMM splits K in two
+    # (two fp32 planes of z, added by the combine in order); the LoRA expand
+    # is added in the first split only
+    spec = workloads.LayerSpec("down_k_split", 4, 2, 128, 8192, 2, [16, 8], [30, 1, 25, 8],
+                               [0, -1, 1, 0], dtype=dtype, seed=27, pool_rank=16)
+    say(f"forward edge: down GEMM K split, I = 8192, {dtype}")
+    inp = gpu_inputs(spec)
+    assert_layer_close(_y32(inp), oracle_forward(inp), dtype, f"down K split {dtype}")
