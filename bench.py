@@ -189,17 +189,20 @@ def counts(spec, meta):
                     ranks[np.maximum(l_of, 0)] if len(ranks) else 0, 0)
     P = T * k
     esz = 2 if spec.dtype == "bf16" else 4
+    fp8 = spec.weights == "fp8"
+    wsz = 1 if fp8 else esz                       # bytes per expert weight
     fl_gate_up_base = 4.0 * H * I * P
     fl_gate_up_expand = 4.0 * float(np.sum(r_of)) * I
     fl_shrink = 4.0 * float(np.sum(r_of)) * H + 2.0 * float(np.sum(r_of)) * I
     fl_down = 2.0 * H * I * P + 2.0 * float(np.sum(r_of)) * H
     total_flops = fl_gate_up_base + fl_gate_up_expand + fl_shrink + fl_down
     active = np.unique(e_of)
-    w_bytes = len(active) * 3.0 * H * I * esz
+    # expert weights (+ their fp32 128 x 128 block scales when fp8)
+    w_bytes = len(active) * 3.0 * H * I * (wsz + (4.0 / (128 * 128) if fp8 else 0.0))
     buckets = set(zip(e_of[r_of > 0].tolist(), l_of[r_of > 0].tolist()))
     lora_bytes = sum(3.0 * ranks[l] * (H + I) * esz for (_, l) in buckets)
     io_bytes = 2.0 * T * H * esz + 8.0 * P
-    gate_up_bytes = len(active) * 2.0 * H * I * esz + T * H * esz
+    gate_up_bytes = len(active) * 2.0 * H * I * (wsz + (4.0 / (128 * 128) if fp8 else 0.0)) + T * H * esz
     return dict(total_flops=total_flops, gate_up_flops=fl_gate_up_base + fl_gate_up_expand,
                 total_bytes=w_bytes + lora_bytes + io_bytes, gate_up_bytes=gate_up_bytes,
                 active_experts=int(len(active)), lora_buckets=len(buckets))
@@ -232,6 +235,22 @@ def cpu_baseline(spec, inp, n_tokens, min_seconds):
         def __getitem__(self, t):
             return xs[int(t)]
 
+    class Fp8View:
+        """fp8 expert weights, dequantized by the oracle one expert at a time"""
+        def __init__(self, codes, scales):
+            self.codes, self.scales = codes, scales
+
+        def __getitem__(self, idx):
+            idx = idx if isinstance(idx, tuple) else (idx,)
+            e = int(idx[0])
+            w = oracle.dequantize_block_fp8(self.codes[e].cpu().numpy(), self.scales[e].cpu().numpy())
+            return w[tuple(int(i) for i in idx[1:])] if len(idx) > 1 else w
+
+    if "w_gate_up_scale" in inp:
+        w_gu = Fp8View(inp["w_gate_up"], inp["w_gate_up_scale"])
+        w_d = Fp8View(inp["w_down"], inp["w_down_scale"])
+    else:
+        w_gu, w_d = View(inp["w_gate_up"]), View(inp["w_down"])
     pools = {n: View(inp[n]) for n in ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
              if n in inp}
     t0 = time.perf_counter()
@@ -239,9 +258,8 @@ def cpu_baseline(spec, inp, n_tokens, min_seconds):
     while passes < 8 and (passes == 0 or time.perf_counter() - t0 < min_seconds):
         en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
                                       m["max_seg_len"])
-        oracle.moe_lora_forward(XView(), m["topk_ids"], m["topk_weights"],
-                                View(inp["w_gate_up"]), View(inp["w_down"]), m["lora_ranks"],
-                                m["scaling"], mp, en, tokens=sample, **pools)
+        oracle.moe_lora_forward(XView(), m["topk_ids"], m["topk_weights"], w_gu, w_d,
+                                m["lora_ranks"], m["scaling"], mp, en, tokens=sample, **pools)
         passes += 1
     dt = time.perf_counter() - t0
     try:
@@ -294,9 +312,11 @@ def main():
     al_ws = torch.empty(binding.moe_lora_align_workspace_bytes(T, k, E, L, BM), dtype=torch.uint8,
                         device=dev)
     y = torch.empty_like(inp["x"])
+    w_scales = ((inp["w_gate_up_scale"], inp["w_down_scale"]) if "w_gate_up_scale" in inp
+                else None)
     fws = torch.empty(binding.moe_lora_forward_workspace_bytes(
         inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"], al, k,
-        inp["lora_ranks"], inp["scaling"], pools), dtype=torch.uint8, device=dev)
+        inp["lora_ranks"], inp["scaling"], pools, w_scales), dtype=torch.uint8, device=dev)
 
     hip = HipEvents()
     nst = len(binding.FORWARD_STAGES)
@@ -309,7 +329,7 @@ def main():
         binding.moe_lora_forward(inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"],
                                  al, k, inp["lora_ranks"] if L > 0 else None,
                                  inp["scaling"] if L > 0 else None, pools, y=y, workspace=fws,
-                                 events=events)
+                                 events=events, w_scales=w_scales)
 
     for _ in range(args.warmup):
         step()
@@ -360,10 +380,18 @@ def main():
         # counters taken on other kernel code say nothing about this one
         if rec.get("source_hash") == kernel_source_hash():
             traffic = rec.get("stages", {}).get("gate_up_gemm", {}).get("bytes")
-    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=traffic,
-                    kernel="gate_up_gemm", kernel_ms=round(gu_ms, 4),
-                    kernel_flops=c["gate_up_flops"])
+    if c["gate_up_flops"] / c["gate_up_bytes"] >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                        frac=round(achieved / peak, 4), traffic=traffic,
+                        kernel="gate_up_gemm", kernel_ms=round(gu_ms, 4),
+                        kernel_flops=c["gate_up_flops"])
+    else:
+        # below the ridge point (decode): the weight stream bounds the kernel
+        gbs = c["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(gbs / PEAK_HBM_GBS, 4), traffic=traffic,
+                        kernel="gate_up_gemm", kernel_ms=round(gu_ms, 4),
+                        kernel_bytes=c["gate_up_bytes"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -382,7 +410,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "dtype": ("bf16" if spec.dtype == "bf16" else "f32") + (" (fp8 e4m3 weights)" if spec.weights == "fp8" else ""),
         "data": "synthetic",
         "config": {"workload": spec.name, "experts": E, "top_k": k, "hidden": spec.hidden,
                    "intermediate": spec.inter, "tokens": T, "requests": spec.num_reqs,

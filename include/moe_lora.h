@@ -51,7 +51,7 @@ enum {
   MOE_LORA_ERR_WORKSPACE = -5    /* workspace missing or too small                      */
 };
 
-typedef enum { MOE_LORA_F32 = 0, MOE_LORA_BF16 = 1 } moe_lora_dtype;
+typedef enum { MOE_LORA_F32 = 0, MOE_LORA_BF16 = 1, MOE_LORA_FP8_E4M3 = 2 } moe_lora_dtype;
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_lora_status_str(int status);
@@ -181,6 +181,24 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
  *                combine result without the final rounding to bf16).
  * num_loras == 0 (pools NULL) runs the plain MoE layer.  H and I must be
  * multiples of 64, R <= 64, top_k <= num_experts.
+ *
+ * FP8 expert weights (the fields after out_dtype; a caller whose struct_size
+ * ends at out_dtype gets weights in `dtype`):
+ *   weight_dtype     `dtype` (0 is read as `dtype` too) or MOE_LORA_FP8_E4M3:
+ *                    w_gate_up and w_down then hold one-byte OCP e4m3 codes
+ *                    (bias 7, no infinities, S.1111.111 = NaN) in the same
+ *                    [E, 2I, H] / [E, H, I] layouts.  Requires dtype BF16 (x,
+ *                    pools and y stay bf16), H and I multiples of 128 and at
+ *                    most 16384.
+ *   w_gate_up_scale  [E, 2I/128, H/128] float32: weight (e, n, k) is
+ *                    code(e, n, k) * scale[e, n/128, k/128] (block-scaled
+ *                    quantization over 128 x 128 blocks of each expert's
+ *                    [rows, K] matrix).
+ *   w_down_scale     [E, H/128, I/128] float32, likewise.
+ * The kernels convert each code exactly and round code * scale to bf16 (exact
+ * for a power-of-two scale) before the bf16 matrix cores; accumulation is fp32.
+ * Errors: MOE_LORA_ERR_UNSUPPORTED for another weight dtype or shape,
+ * MOE_LORA_ERR_INVALID for a missing scale pointer.
  */
 typedef struct moe_lora_forward_args {
   size_t struct_size; /* sizeof(moe_lora_forward_args) */
@@ -208,6 +226,9 @@ typedef struct moe_lora_forward_args {
   size_t workspace_bytes;
   void* y;
   int32_t out_dtype; /* moe_lora_dtype of y */
+  int32_t weight_dtype;           /* moe_lora_dtype of w_gate_up / w_down */
+  const float* w_gate_up_scale;   /* FP8_E4M3 weights: [E, 2I/128, H/128] */
+  const float* w_down_scale;      /* FP8_E4M3 weights: [E, H/128, I/128] */
 } moe_lora_forward_args;
 
 /* Workspace bytes moe_lora_forward needs for the sizes in `args` (0 if invalid). */

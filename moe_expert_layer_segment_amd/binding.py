@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LORA_LIB") or os.path.join(_PKG, "lib", "libmoe_lora.so")
 
 OK, ERR_INVALID, ERR_UNDERCOVER, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
-DTYPE_F32, DTYPE_BF16 = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+_FP8_TORCH = (torch.uint8, torch.float8_e4m3fn)   # one-byte e4m3 codes
 FORWARD_STAGES = ("plan", "shrink_gate_up", "gate_up_gemm", "shrink_down", "down_gemm", "combine")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -41,6 +42,8 @@ class ForwardArgs(ctypes.Structure):
         ("num_rows_padded", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("y", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32),
+        ("w_gate_up_scale", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p),
     ]
 
 
@@ -235,7 +238,7 @@ _POOLS = ("a_gate", "a_up", "b_gate", "b_up", "a_down", "b_down")
 
 
 def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
-                  top_k, y, workspace, out_dtype=None) -> ForwardArgs:
+                  top_k, y, workspace, out_dtype=None, w_scales=None) -> ForwardArgs:
     T, H = x.shape
     E, twoI, H2 = w_gate_up.shape
     I = twoI // 2
@@ -247,10 +250,22 @@ def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, sca
         raise TypeError(f"unsupported dtype {x.dtype}")
     dev = x.device
     _need(x, "x", x.dtype)
-    _need(w_gate_up, "w_gate_up", x.dtype, dev)
-    _need(w_down, "w_down", x.dtype, dev)
+    fp8 = w_gate_up.dtype in _FP8_TORCH
+    wdt = w_gate_up.dtype if fp8 else x.dtype
+    _need(w_gate_up, "w_gate_up", wdt, dev)
+    _need(w_down, "w_down", wdt, dev)
     if H2 != H or tuple(w_down.shape) != (E, H, I):
         raise ValueError("weight shapes do not match x / each other")
+    if fp8:
+        if x.dtype != torch.bfloat16:
+            raise TypeError("fp8 expert weights need bf16 activations")
+        if w_scales is None:
+            raise ValueError("fp8 expert weights need their block scales (w_scales)")
+        sgu, sd = w_scales
+        _need(sgu, "w_gate_up_scale", torch.float32, dev)
+        _need(sd, "w_down_scale", torch.float32, dev)
+        if tuple(sgu.shape) != (E, 2 * I // 128, H // 128) or tuple(sd.shape) != (E, H // 128, I // 128):
+            raise ValueError("block scales must be [E, 2I/128, H/128] and [E, H/128, I/128]")
     _need(topk_weights, "topk_weights", torch.float32, dev, T * top_k)
     L, R = 0, 0
     if pools is not None:
@@ -279,6 +294,9 @@ def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, sca
     a.num_loras, a.max_rank, a.block_m = L, R, int(align_out["block_m"])
     a.x, a.topk_weights = x.data_ptr(), topk_weights.data_ptr()
     a.w_gate_up, a.w_down = w_gate_up.data_ptr(), w_down.data_ptr()
+    if fp8:
+        a.weight_dtype = DTYPE_FP8_E4M3
+        a.w_gate_up_scale, a.w_down_scale = w_scales[0].data_ptr(), w_scales[1].data_ptr()
     if pools is not None:
         for n in _POOLS:
             setattr(a, n, pools[n].data_ptr())
@@ -296,9 +314,10 @@ def _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, sca
 
 
 def moe_lora_forward_workspace_bytes(x, topk_weights, w_gate_up, w_down, align_out, top_k,
-                                     lora_ranks=None, scaling=None, pools=None) -> int:
+                                     lora_ranks=None, scaling=None, pools=None,
+                                     w_scales=None) -> int:
     a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
-                      top_k, None, None)
+                      top_k, None, None, w_scales=w_scales)
     n = int(lib().moe_lora_forward_workspace_bytes(ctypes.byref(a)))
     if n == 0:
         raise MoeLoraError(ERR_INVALID, "moe_lora_forward_workspace_bytes")
@@ -312,8 +331,12 @@ def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: tor
                      pools: Optional[Dict[str, torch.Tensor]] = None,
                      y: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     events=None, out_dtype=None) -> torch.Tensor:
+                     events=None, out_dtype=None, w_scales=None) -> torch.Tensor:
     """The MoE-LoRA layer: returns y [T, H] (written into ``y`` if given).
+
+    fp8 expert weights: ``w_gate_up`` / ``w_down`` as uint8 or float8_e4m3fn
+    e4m3 codes and ``w_scales`` = (gate_up scales [E, 2I/128, H/128], down
+    scales [E, H/128, I/128]), float32.
 
     ``events``: optional sequence of 2 * len(FORWARD_STAGES) raw hipEvent_t
     handles recorded around each kernel stage (measurement only).
@@ -323,10 +346,10 @@ def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: tor
                         device=x.device)
     if workspace is None:
         n = moe_lora_forward_workspace_bytes(x, topk_weights, w_gate_up, w_down, align_out, top_k,
-                                             lora_ranks, scaling, pools)
+                                             lora_ranks, scaling, pools, w_scales)
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
     a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
-                      top_k, y, workspace, out_dtype)
+                      top_k, y, workspace, out_dtype, w_scales)
     if events is None:
         _check(lib().moe_lora_forward(ctypes.byref(a), _stream()), "moe_lora_forward")
     else:
@@ -350,6 +373,9 @@ def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True,
                            max_len=inputs["meta"]["max_seg_len"])
     al = moe_lora_align(inputs["topk_ids"], mp, en if L > 0 else None, E, L, block_m)
     pools = {n: inputs[n] for n in _POOLS} if L > 0 else None
+    ws = ((inputs["w_gate_up_scale"], inputs["w_down_scale"])
+          if "w_gate_up_scale" in inputs else None)
     return moe_lora_forward(inputs["x"], inputs["topk_weights"], inputs["w_gate_up"],
                             inputs["w_down"], al, k, ranks if L > 0 else None,
-                            inputs["scaling"] if L > 0 else None, pools, out_dtype=out_dtype)
+                            inputs["scaling"] if L > 0 else None, pools, out_dtype=out_dtype,
+                            w_scales=ws)

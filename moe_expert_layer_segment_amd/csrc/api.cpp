@@ -1,5 +1,6 @@
 // C ABI of the MoE-LoRA library: host-side validation (host scalars only) and
 // dispatch to the HIP launchers.  See include/moe_lora.h for the contract.
+#include <cstddef>
 #include "moe_lora.h"
 
 #include <hip/hip_runtime.h>
@@ -97,7 +98,12 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
 }
 
 static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool check_ptrs) {
-  if (!a || a->struct_size < sizeof(moe_lora_forward_args)) return MOE_LORA_ERR_INVALID;
+  // the fields up to out_dtype are required; the fp8 weight fields are read
+  // when struct_size covers them
+  constexpr size_t kBaseSize = offsetof(moe_lora_forward_args, out_dtype) + sizeof(int32_t);
+  if (!a || a->struct_size < kBaseSize) return MOE_LORA_ERR_INVALID;
+  const bool has_w = a->struct_size >= sizeof(moe_lora_forward_args);
+  const int32_t wdt = has_w && a->weight_dtype != 0 ? a->weight_dtype : a->dtype;
   if (a->dtype != MOE_LORA_F32 && a->dtype != MOE_LORA_BF16) return MOE_LORA_ERR_UNSUPPORTED;
   if (a->num_tokens < 0 || a->hidden <= 0 || a->inter <= 0 || a->num_experts <= 0 ||
       a->top_k <= 0 || a->num_loras < 0 || a->max_rank < 0 || bad_block_m(a->block_m))
@@ -128,6 +134,17 @@ static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool ch
   p->y = a->y;
   if (a->out_dtype != a->dtype && a->out_dtype != MOE_LORA_F32) return MOE_LORA_ERR_UNSUPPORTED;
   p->out_f32 = (a->out_dtype == MOE_LORA_F32) && a->dtype != MOE_LORA_F32;
+  p->wdtype = 0;
+  if (wdt != a->dtype) {
+    if (wdt != MOE_LORA_FP8_E4M3 || a->dtype != MOE_LORA_BF16) return MOE_LORA_ERR_UNSUPPORTED;
+    if (a->hidden % 128 || a->inter % 128 || a->hidden > 16384 || a->inter > 16384)
+      return MOE_LORA_ERR_UNSUPPORTED;
+    if (check_ptrs && a->num_tokens > 0 && (!a->w_gate_up_scale || !a->w_down_scale))
+      return MOE_LORA_ERR_INVALID;
+    p->wdtype = kWeightFp8;
+    p->w_gate_up_scale = a->w_gate_up_scale;
+    p->w_down_scale = a->w_down_scale;
+  }
   return MOE_LORA_OK;
 }
 

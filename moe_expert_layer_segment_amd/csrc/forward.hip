@@ -437,8 +437,9 @@ struct GemmArgs {
   const int32_t* sorted_ids;
   int top_k, P;
   int64_t K;
-  // B operand: weights [E, w_rows, K]
-  const T* w;
+  // B operand: weights [E, w_rows, K], in T or as fp8 e4m3 codes
+  const void* w;
+  const float* w_scale;       // fp8 weights: [E, w_rows/128, K/128] block scales, else null
   int64_t n_out;              // output columns (I for gate_up, H for down)
   int64_t w_rows;             // rows per expert of w (2I or H)
   // LoRA
@@ -491,6 +492,28 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t
       : "memory");
 }
 
+// 16 fp8 e4m3 codes (4 dwords, element 4w+b = byte b of dword w) times a
+// block scale, as two bf16x8 fragments: elements 0..7 and 8..15.  The code
+// itself converts exactly (every e4m3 value is a bf16 value); the product
+// with the scale is rounded to nearest-even bf16 (exact for a power-of-two
+// scale).
+__device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bf16x8& lo, bf16x8& hi) {
+  typedef float float2v __attribute__((ext_vector_type(2)));
+  float f[16];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2v p0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], false);
+    const float2v p1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[w], true);
+    f[4 * w + 0] = p0[0]; f[4 * w + 1] = p0[1];
+    f[4 * w + 2] = p1[0]; f[4 * w + 3] = p1[1];
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    lo[v] = (bf16_t)(f[v] * sc);
+    hi[v] = (bf16_t)(f[8 + v] * sc);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   // all of this wave's LDS loads except the newest N have landed, then every
@@ -499,7 +522,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int ROWB, bool GATE_UP>
+// W: weight element, T (bf16 / fp32 weights) or uint8_t (fp8 e4m3 codes with
+// 128 x 128 block scales; T = bf16)
+template <typename T, typename W, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int ROWB, bool GATE_UP>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T> a) {
   typedef Elt<T> E_;
   typedef Blk<T> B_;
@@ -512,10 +537,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   constexpr int RPS = 1024 / ROWB;                // rows per 1 KB DMA segment
   static_assert(ROWB == 64 || ROWB == 128, "row size");
   constexpr int NWAVES = WAVES_M * WAVES_N;
-  constexpr int ROWS = BM + BN;                   // LDS rows per stage: A rows then B rows
-  constexpr int SEGS = ROWS / RPS;                // 1 KB segments per stage
+  constexpr bool WF8 = sizeof(W) == 1;            // fp8 weights: B rows hold BK one-byte codes
+  static_assert(!WF8 || (sizeof(T) == 2 && ROWB == 128), "fp8 weights with bf16 activations");
+  constexpr int ROWB_B = WF8 ? ROWB / 2 : ROWB;   // bytes per LDS row of B
+  constexpr int CPR_B = ROWB_B / 16, RPS_B = 1024 / ROWB_B;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB_B;
+  constexpr int A_SEGS = A_BYTES / 1024;          // stage: A rows, then B rows
+  constexpr int SEGS = (A_BYTES + B_BYTES) / 1024;  // 1 KB segments per stage
   constexpr int SEG_PER_WAVE = SEGS / NWAVES;     // DMA instructions per wave per stage
-  constexpr int STAGE_BYTES = ROWS * ROWB;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
   constexpr int MB = WM / BS, NB = WN / BS;
   constexpr int KSUB = BK / KF;
@@ -526,6 +556,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
   __shared__ int ep_pid[BM];      // down epilogue: pair id of each tile row
   __shared__ float ep_w[BM];      // and its router weight
+  // fp8 weights: each wave's block scales for the tile's K range, [wave][j][K/128]
+  constexpr int MAXKB = 128;      // K / 128 per tile (K <= 16384)
+  __shared__ float sc_lds[WF8 ? NWAVES * NB * MAXKB : 1];
 
   // Persistent tile loop.  Logical tiles are ordered expert by expert, and
   // inside an expert by groups of its work items, column-major with the
@@ -611,8 +644,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   auto swz = [](int row) -> int {
     return ROWB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
   };
+  // B rows: 64-byte rows (fp8) swizzle like 64-byte A rows would
+  auto swzb = [](int n) -> int {
+    return ROWB_B == 128 ? ((n >> 1) & 7) : ((n >> 2) & 3);
+  };
   const T* a_base = a.a_src;
-  const T* b_base = a.w + (int64_t)e * a.w_rows * a.K;
+  const W* b_base = static_cast<const W*>(a.w) + (int64_t)e * a.w_rows * a.K;
   // global row (of a_base for row < BM, of b_base otherwise) behind LDS row `row`
   auto grow_of = [&](int row, int pid_in) -> int64_t {
     if (row < BM) {
@@ -643,9 +680,16 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 #pragma unroll
   for (int i = 0; i < SEG_PER_WAVE; ++i) {
     const int seg = wave * SEG_PER_WAVE + i;
-    const int row = seg * RPS + lane / CPR;
-    const int kc = (lane % CPR) ^ swz(row);
-    src_off[i] = (uint32_t)((grow_of(row, pidv[i]) * a.K + kc * E_::kChunk) * sizeof(T));
+    if (seg < A_SEGS) {
+      const int row = seg * RPS + lane / CPR;
+      const int kc = (lane % CPR) ^ swz(row);
+      src_off[i] = (uint32_t)((grow_of(row, pidv[i]) * a.K + kc * E_::kChunk) * sizeof(T));
+    } else {
+      // B row n of the stage (LDS row BM + n; swz(BM + n) == swzb(n) as BM % 16 == 0)
+      const int n = (seg - A_SEGS) * RPS_B + lane / CPR_B;
+      const int kc = (lane % CPR_B) ^ swzb(n);
+      src_off[i] = (uint32_t)(grow_of(BM + n, 0) * a.K * (int64_t)sizeof(W) + kc * 16);
+    }
   }
   // Publish the next claim now: every wave read the current one before the
   // barrier above, and the K loop's barriers make this write visible before
@@ -658,12 +702,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // this wave's DMA instructions [I0, I1) of one stage
   auto issue_part = [&](auto i0_c, auto i1_c, int stage_k, int buf) {
     constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
-    const uint32_t kbytes = (uint32_t)((int64_t)split * (kper / BK) + stage_k) * ROWB;
+    const uint32_t ktile = (uint32_t)((int64_t)split * (kper / BK) + stage_k);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const int seg = wave * SEG_PER_WAVE + i;
-      const void* base = (seg * RPS < BM) ? (const void*)a_base : (const void*)b_base;
-      dma16(base, src_off[i] + kbytes, lds_u32 + buf * STAGE_BYTES + seg * 1024);
+      const bool is_a = seg < A_SEGS;
+      const void* base = is_a ? (const void*)a_base : (const void*)b_base;
+      dma16(base, src_off[i] + ktile * (is_a ? ROWB : ROWB_B), lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
   };
   const int nk = (int)(kper / BK);
@@ -690,6 +735,20 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   auto col_of = [&](int j) -> int64_t {
     if (GATE_UP) return n0 + wn * (WN / 2) + (j % (NB / 2)) * BS;
     return n0 + wn * WN + j * BS;
+  };
+  // fp8 weights: this wave's block scales of the tile's K range into sc_lds
+  // (the wave reads only its own entries, so no barrier is needed)
+  auto fill_scales = [&]() {
+    const int nkb = (int)(kper / 128);
+    const int64_t kbs = a.K / 128, rows128 = a.w_rows / 128;
+    for (int idx = lane; idx < NB * nkb; idx += 64) {
+      const int j = idx / nkb, kb = idx - j * nkb;
+      const int64_t col = col_of(j);
+      int64_t wrow = (GATE_UP && j >= NB / 2) ? a.n_out + col : col;
+      wrow = min(wrow, a.w_rows - 1);
+      sc_lds[(wave * NB + j) * MAXKB + kb] =
+          a.w_scale[((int64_t)e * rows128 + wrow / 128) * kbs + (int64_t)split * nkb + kb];
+    }
   };
   // LDS row of B for this lane in column block j
   auto b_row_of = [&](int j) -> int {
@@ -737,12 +796,30 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // Fragments are double-buffered in registers: the LDS reads of sub-step
   // ks+1 are issued before the MFMAs of sub-step ks.
   frag fa[2][MB], fb[2][NB];
+  // fp8 weights: a lane's 8 K elements of sub-step ks are K offsets
+  // 32*(ks/2) + 16*h + 8*(ks%2) (h = lane half), the same for A and B, so one
+  // 16-byte read of a B row serves sub-steps ks and ks+1.  fbq[pair][half][j]
+  // holds the converted fragments; sck[j] the K tile's block scales.
+  frag fbq[2][2][NB];
+  float sck[NB];
   auto load_frags = [&](const char* base, int ks, int set) {
-    const int kel = ks * KF + lk;
+    const int kel = WF8 ? 32 * (ks >> 1) + 2 * lk + 8 * (ks & 1) : ks * KF + lk;
 #pragma unroll
     for (int i = 0; i < MB; ++i) fa[set][i] = lfrag(base, wm * WM + i * BS + lrow, kel);
+    if constexpr (!WF8) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) fb[set][j] = lfrag(base, b_row_of(j), kel);
+      for (int j = 0; j < NB; ++j) fb[set][j] = lfrag(base, b_row_of(j), kel);
+    } else {
+      if ((ks & 1) == 0) {
+        const int kc = 2 * (ks >> 1) + (lk >> 3);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = b_row_of(j) - BM;
+          const int4v raw = *reinterpret_cast<const int4v*>(base + A_BYTES + n * ROWB_B + ((kc ^ swzb(n)) * 16));
+          fp8x16_to_bf16(raw, sck[j], fbq[(ks >> 1) & 1][0][j], fbq[(ks >> 1) & 1][1][j]);
+        }
+      }
+    }
   };
   // ---- main loop: STAGES-deep LDS ring fed by DMA, one barrier per K tile --
   // Step s: wait for this wave's loads of tile s, barrier (everyone's tile s
@@ -756,12 +833,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // uniform).
   auto main_loop = [&](auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
-    auto mma_frags = [&](int set) {
+    auto mma_frags = [&](int ks) {
+      const int set = ks & 1;
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         if (!FULL && wm * WM + i * BS >= nrows) continue;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = B_::mma(fa[set][i], fb[set][j], acc[i][j]);
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = B_::mma(fa[set][i], WF8 ? fbq[(ks >> 1) & 1][ks & 1][j] : fb[set][j], acc[i][j]);
       }
     };
     // Multiply the stage in ring slot buf; when next_k >= 0 also issue the
@@ -769,8 +848,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     // Instruction order is pinned with scheduling barriers: the fragment
     // reads of sub-step ks+1 and a share of the DMA go out before the MFMAs
     // of sub-step ks, so LDS latency and DMA issue hide behind MFMA work.
-    auto compute = [&](int buf, int next_k, int next_buf) {
+    auto compute = [&](int buf, int next_k, int next_buf, int kt) {
       const char* base = lds + buf * STAGE_BYTES;
+      if constexpr (WF8) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sck[j] = sc_lds[(wave * NB + j) * MAXKB + (kt * BK) / 128];
+      }
       load_frags(base, 0, 0);
       static_for<KSUB>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
@@ -782,23 +865,24 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ks + 1 < KSUB) load_frags(base, ks + 1, (ks + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
-        mma_frags(ks & 1);
+        mma_frags(ks);
       });
       __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
       if (st < nk) issue_stage(st, st);
+    if constexpr (WF8) fill_scales();
     int s = 0;
     // steady state: STAGES-1 tiles are in flight at each wait
     for (; s + STAGES - 1 < nk; ++s) {
       wait_vm_barrier<(STAGES - 2) * SEG_PER_WAVE>();
-      compute(s % STAGES, s + STAGES - 1, (s + STAGES - 1) % STAGES);
+      compute(s % STAGES, s + STAGES - 1, (s + STAGES - 1) % STAGES, s);
     }
     // drain: no more loads to issue
     for (; s < nk; ++s) {
       wait_vm_barrier<0>();
-      compute(s % STAGES, -1, 0);
+      compute(s % STAGES, -1, 0, s);
     }
   };
   if (wm * WM + WM <= nrows)
@@ -1037,6 +1121,15 @@ template <> struct TileCfg<bf16_t> {
                        ROWB = MOELORA_BF16_ROWB, PER_CU = 1;
   static constexpr int BN_DOWN = MOELORA_BF16_BN_DOWN, STAGES_DOWN = MOELORA_BF16_STAGES_DOWN;
 };
+// fp8 e4m3 weights (bf16 activations): the same tile; the B half of a stage
+// is half as large (32 KB stages), so the ring is 4 deep (128 KB, which also
+// holds the down epilogue's fp32 staging)
+struct Fp8Cfg {
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 4, ROWB = 128, PER_CU = 1;
+};
+static_assert(Fp8Cfg::BM == TileCfg<bf16_t>::BM && Fp8Cfg::BN == TileCfg<bf16_t>::BN &&
+                  Fp8Cfg::BN == TileCfg<bf16_t>::BN_DOWN,
+              "fp8 tiles share the work items and column tiles of the bf16 path");
 template <> struct TileCfg<float> {
   static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, ROWB = 128, PER_CU = 2;
   static constexpr int BN_DOWN = 64, STAGES_DOWN = 3;
@@ -1056,12 +1149,13 @@ static int64_t gemm_grid(int64_t tiles, int per_cu) {
 // (one item per BM pairs plus a partial one per expert), so the choice, and
 // with it the rounding of y, does not depend on the align block size.
 template <typename T>
-static int down_ksplit(int64_t P, int64_t E, int64_t H, int64_t I) {
+static int down_ksplit(int64_t P, int64_t E, int64_t H, int64_t I, bool fp8) {
   constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN_DOWN, BK = TileCfg<T>::ROWB / (int)sizeof(T);
   const int64_t items = ceil_div(P, BM) + std::min(P, E);
   const int64_t tiles = items * ceil_div(H, BN);
   const int64_t slots = 256 * (int64_t)TileCfg<T>::PER_CU;
-  if (P <= 0 || I % (2 * BK) != 0 || I / 2 < 4096 || tiles >= 8 * slots) return 1;
+  const int64_t kalign = fp8 ? 128 : BK;   // a split holds whole K tiles (and whole scale blocks)
+  if (P <= 0 || I % (2 * kalign) != 0 || I / 2 < 4096 || tiles >= 8 * slots) return 1;
   return 2;
 }
 
@@ -1128,7 +1222,8 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
-  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I) : down_ksplit<float>(P, p.E, p.H, p.I);
+  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
+                                : down_ksplit<float>(P, p.E, p.H, p.I, false);
   w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
   w.bytes = off;
   return w;
@@ -1152,6 +1247,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   const int64_t P = p.T * p.k;
   const bool lora = p.L > 0;
   constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN;
+  constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+  const bool fp8w = kBf16 && p.wdtype == kWeightFp8;
 
   mark(2 * kStagePlan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, (int)p.E, (int)p.BM, BM,
@@ -1208,7 +1305,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     GemmArgs<T> a = g;
     a.a_src = static_cast<const T*>(p.x);
     a.K = p.H;
-    a.w = static_cast<const T*>(p.w_gate_up);
+    a.w = p.w_gate_up;
+    a.w_scale = fp8w ? p.w_gate_up_scale : nullptr;
     a.n_out = p.I;
     a.w_rows = 2 * p.I;
     a.n_cols = (int)ceil_div(p.I, BN / 2);
@@ -1222,8 +1320,16 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.tile_ctr = count + 4;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
-                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
+    if constexpr (kBf16) {
+      if (fp8w) {
+        typedef Fp8Cfg F;
+        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+      }
+    }
+    if (!fp8w)
+      hipLaunchKernelGGL((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
+                         dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageGateUp + 1);
   }
   mark(2 * kStageShrinkA);
@@ -1259,7 +1365,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     GemmArgs<T> a = g;
     a.a_src = act;
     a.K = p.I;
-    a.w = static_cast<const T*>(p.w_down);
+    a.w = p.w_down;
+    a.w_scale = fp8w ? p.w_down_scale : nullptr;
     a.n_out = p.H;
     a.w_rows = p.H;
     constexpr int BND = TileCfg<T>::BN_DOWN, SD = TileCfg<T>::STAGES_DOWN;
@@ -1274,8 +1381,16 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.tile_ctr = count + 12;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
-                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
+    if constexpr (kBf16) {
+      if (fp8w) {
+        typedef Fp8Cfg F;
+        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+      }
+    }
+    if (!fp8w)
+      hipLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
+                         dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
     mark(2 * kStageDown + 1);
   }
   mark(2 * kStageCombine);

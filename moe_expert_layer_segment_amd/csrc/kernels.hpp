@@ -40,8 +40,14 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
                         hipStream_t stream);
 
 // ---- forward ---------------------------------------------------------------
+// expert weights as fp8 e4m3 codes with 128 x 128 block scales (dtype bf16)
+constexpr int kWeightFp8 = 2;
+
 struct ForwardProblem {
   int dtype;  // 0 = fp32, 1 = bf16
+  int wdtype = 0;  // dtype of the expert weights: dtype, or kWeightFp8
+  const float* w_gate_up_scale = nullptr;   // fp8: [E, 2I/128, H/128]
+  const float* w_down_scale = nullptr;      // fp8: [E, H/128, I/128]
   int64_t T, H, I, E, k, L, R, BM;
   const void* x;
   const float* topk_weights;

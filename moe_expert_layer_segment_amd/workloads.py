@@ -22,6 +22,10 @@ silent:
   stored as float32.
 * Each tensor (and each expert slice of it) has its own sub-seed derived from
   ``(seed, tensor_id, expert)``, so any expert can be regenerated on its own.
+* fp8 expert weights (``weights="fp8"``): each expert's fp32 draw is quantized
+  to OCP e4m3 codes over 128 x 128 blocks with scale = block amax / 448 (the
+  largest finite e4m3 value), the usual block-scaled recipe; x, pools and y
+  stay bf16.
 """
 from __future__ import annotations
 
@@ -54,6 +58,7 @@ class LayerSpec:
     router: str = "normal"       # "normal" | "zipf" | "uniform_bias"
     alpha_over_rank: float = 2.0  # scaling = alpha / r with alpha = 2r
     pool_rank: Optional[int] = None
+    weights: str = "same"        # "same" (dtype) or "fp8": e4m3 codes + 128 x 128 block scales
 
     @property
     def num_tokens(self) -> int:
@@ -155,10 +160,16 @@ def config(name: str) -> LayerSpec:
         lens, wi = c4.seg_lens, c4.weight_indices
         return LayerSpec(f"{name}_rank", 32, 1, c4.hidden, c4.inter, c4.num_loras, c4.lora_ranks,
                          lens, wi, seed=c4.seed, router="uniform_bias", pool_rank=c4.pool_rank)
+    if name.endswith("_fp8") and name[:-4] in ("c1", "c3", "c4p", "c4d"):
+        # the same layer and batch with fp8 e4m3 expert weights
+        base = config(name[:-4])
+        return dataclasses.replace(base, name=base.name + "_fp8", weights="fp8")
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("c0", "c1", "c2", "c3", "c4p", "c4d")
+# the quantized-weight variants (fp8 e4m3 base weights, bf16 LoRA)
+FP8_CONFIG_NAMES = ("c1_fp8", "c3_fp8", "c4p_fp8", "c4d_fp8")
 # one rank's share of a layer under tensor / expert parallelism (shapes only)
 SHARD_CONFIG_NAMES = ("c1_tp8", "c4p_ep8", "c4d_ep8")
 
@@ -199,6 +210,19 @@ def route(logits: np.ndarray, k: int):
 # ----------------------------------------------------------------------------
 # tensors
 # ----------------------------------------------------------------------------
+def quantize_fp8_blocks(w: torch.Tensor, block: int = 128):
+    """Input preparation for fp8 weights: a float [N, K] matrix as (OCP e4m3
+    codes uint8 [N, K], float32 scales [N / block, K / block]) with
+    scale = block amax / 448 (1 for an all-zero block) and code = the e4m3
+    rounding of w / scale."""
+    N, K = w.shape
+    b = w.float().reshape(N // block, block, K // block, block)
+    amax = b.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (b / scale[:, None, :, None]).reshape(N, K).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), scale
+
+
 def _randn(shape, std: float, seed: int, device, dtype) -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -233,11 +257,25 @@ def generate(spec: LayerSpec, device="cpu", canary: bool = True,
     out: Dict[str, object] = {}
     x_key = 0 if not spec.name.startswith("c4d") else 1
     out["x"] = _randn((T, H), 1.0, _subseed(s, _TID_X, x_key), dev, dt)
-    wgu = torch.empty((E, 2 * I, H), device=dev, dtype=dt)
-    wd = torch.empty((E, H, I), device=dev, dtype=dt)
-    for e in range(E):
-        wgu[e] = _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, dt)
-        wd[e] = _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, dt)
+    if spec.weights == "fp8":
+        if dt != torch.bfloat16:
+            raise ValueError("fp8 expert weights go with bf16 activations")
+        wgu = torch.empty((E, 2 * I, H), device=dev, dtype=torch.uint8)
+        wd = torch.empty((E, H, I), device=dev, dtype=torch.uint8)
+        sgu = torch.empty((E, 2 * I // 128, H // 128), device=dev, dtype=torch.float32)
+        sd = torch.empty((E, H // 128, I // 128), device=dev, dtype=torch.float32)
+        for e in range(E):
+            wgu[e], sgu[e] = quantize_fp8_blocks(
+                _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, torch.float32))
+            wd[e], sd[e] = quantize_fp8_blocks(
+                _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, torch.float32))
+        out["w_gate_up_scale"], out["w_down_scale"] = sgu, sd
+    else:
+        wgu = torch.empty((E, 2 * I, H), device=dev, dtype=dt)
+        wd = torch.empty((E, H, I), device=dev, dtype=dt)
+        for e in range(E):
+            wgu[e] = _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, dt)
+            wd[e] = _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, dt)
     out["w_gate_up"], out["w_down"] = wgu, wd
 
     if with_lora and L > 0:

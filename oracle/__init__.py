@@ -7,6 +7,8 @@ code with the HIP path.
 from .moe_lora_oracle import (  # noqa: F401
     UnderCoverError,
     align_capacity_rows,
+    decode_e4m3,
+    dequantize_block_fp8,
     moe_lora_align,
     moe_lora_forward,
     moe_lora_forward_bruteforce,

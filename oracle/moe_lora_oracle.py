@@ -329,3 +329,35 @@ def moe_lora_route(logits, top_k: int):
         e = np.exp(top - top[0])
         w[t] = e / e.sum()
     return ids, w
+
+
+# ---------------------------------------------------------------------------
+# fp8 expert weights (the quantized-MoE-LoRA variant: fp8 base weights, bf16
+# LoRA).  Format: OCP 8-bit floating point, E4M3 -- 1 sign bit, 4 exponent
+# bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+# m * 2^-9; no infinities; S.1111.111 is NaN, so the largest finite value is
+# 1.75 * 2^8 = 448.  Block scaling: weight (e, n, k) = code * scale[e, n / 128,
+# k / 128] over 128 x 128 blocks of each expert's [rows, K] matrix.
+# ---------------------------------------------------------------------------
+def decode_e4m3(codes) -> np.ndarray:
+    """float64 values of OCP E4M3 codes (uint8 array of any shape)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
+    subnormal = man * 2.0 ** -9
+    v = sign * np.where(exp == 0, subnormal, normal)
+    return np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, v)
+
+
+def dequantize_block_fp8(codes, scales, block: int = 128) -> np.ndarray:
+    """float64 weights from E4M3 codes [..., N, K] and block scales
+    [..., N / block, K / block]: each code times the scale of its block."""
+    w = decode_e4m3(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    n, k = w.shape[-2], w.shape[-1]
+    if n % block or k % block or s.shape[-2:] != (n // block, k // block):
+        raise ValueError("codes and scales do not tile into blocks")
+    s_full = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)
+    return w * s_full

@@ -36,6 +36,33 @@ class HostView:
         return self.t[key].float().cpu().numpy().astype(np.float64)
 
 
+class Fp8HostView:
+    """fp8 e4m3 expert weights seen by the oracle: each expert's codes and
+    block scales copied to the host and dequantized by the oracle on access
+    (the last expert is kept, since the oracle reads one expert at a time)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        self.codes, self.scales = codes, scales
+        self._e, self._w = None, None
+
+    def __getitem__(self, idx):
+        key = idx if isinstance(idx, tuple) else (idx,)
+        e = int(key[0])
+        if self._e != e:
+            self._w = oracle.dequantize_block_fp8(self.codes[e].cpu().numpy(),
+                                                  self.scales[e].cpu().numpy())
+            self._e = e
+        return self._w[tuple(int(i) for i in key[1:])] if len(key) > 1 else self._w
+
+
+def weight_views(inp: dict):
+    """(w_gate_up, w_down) host views for the oracle, dequantizing fp8 weights."""
+    if "w_gate_up_scale" in inp:
+        return (Fp8HostView(inp["w_gate_up"], inp["w_gate_up_scale"]),
+                Fp8HostView(inp["w_down"], inp["w_down_scale"]))
+    return HostView(inp["w_gate_up"]), HostView(inp["w_down"])
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype in (torch.int32, torch.int64):
         return t.cpu().numpy()
@@ -48,9 +75,10 @@ def oracle_forward(inp: dict, tokens=None, with_lora=True):
     T = inp["x"].shape[0]
     en, mp = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"], m["lora_ranks"],
                                   m["max_seg_len"])
+    w_gu, w_d = weight_views(inp)
     kw = dict(x=to_np(inp["x"]) if tokens is None else HostView(inp["x"]),
               topk_ids=m["topk_ids"], topk_weights=m["topk_weights"],
-              w_gate_up=HostView(inp["w_gate_up"]), w_down=HostView(inp["w_down"]),
+              w_gate_up=w_gu, w_down=w_d,
               lora_ranks=m["lora_ranks"], scaling=m["scaling"],
               token_lora_mapping=mp, adapter_enabled=en, tokens=tokens)
     if with_lora and "a_gate" in inp:

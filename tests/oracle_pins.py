@@ -459,4 +459,58 @@ def pin_route_closed_forms(orc):
     assert list(ids[0]) == [1, 0] and np.allclose(w[0], [1 / (1 + np.exp(-1.0)), 1 / (1 + np.exp(1.0))])
 
 
+# ---------------------------------------------------------------------------
+# fp8 expert weights: OCP E4M3 codes with 128 x 128 block scales
+# ---------------------------------------------------------------------------
+# code -> value from the format's definition (sign, 4-bit exponent with bias 7,
+# 3-bit mantissa, exponent field 0 = subnormal m * 2^-9, S.1111.111 = NaN)
+_E4M3_TABLE = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+    0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x3F: 1.875, 0x40: 2.0, 0x48: 4.0,
+    0x70: 128.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+    0x81: -(2.0 ** -9), 0xB8: -1.0, 0xC0: -2.0, 0xFE: -448.0,
+}
+
+
+def pin_e4m3_closed_forms(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.decode_e4m3(codes)
+    for c, want in _E4M3_TABLE.items():
+        assert v[c] == want, (hex(c), v[c], want)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    # the finite positive codes are strictly increasing, the negative ones mirror them
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+
+
+def pin_e4m3_vs_torch(orc):
+    # an independent implementation of the same format
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    v = orc.decode_e4m3(codes)
+    same = (v == ref) | (np.isnan(v) & np.isnan(ref))
+    assert same.all(), np.nonzero(~same)
+
+
+def pin_block_dequant(orc):
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 256, size=(2, 256, 384), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A          # no NaN codes
+    scales = rng.uniform(0.01, 3.0, size=(2, 2, 3))
+    w = orc.dequantize_block_fp8(codes, scales)
+    assert w.shape == codes.shape
+    vals = orc.decode_e4m3(codes)
+    for _ in range(200):
+        e, n, k = int(rng.integers(2)), int(rng.integers(256)), int(rng.integers(384))
+        assert w[e, n, k] == vals[e, n, k] * scales[e, n // 128, k // 128], (e, n, k)
+    # one block's scale moves exactly that block
+    s2 = scales.copy()
+    s2[1, 0, 2] *= 2.0
+    d = orc.dequantize_block_fp8(codes, s2) != w
+    mask = np.zeros_like(d)
+    mask[1, 0:128, 256:384] = vals[1, 0:128, 256:384] != 0
+    assert np.array_equal(d, mask)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -125,7 +125,7 @@ def _fargs(**over):
     for n, _ in binding.ForwardArgs._fields_:
         if n not in ("struct_size", "dtype", "num_tokens", "hidden", "inter", "num_experts",
                      "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes",
-                     "out_dtype"):
+                     "out_dtype", "weight_dtype"):
             setattr(a, n, 0x1000)
     a.workspace_bytes = 1
     a.out_dtype = binding.DTYPE_BF16
@@ -156,11 +156,36 @@ def test_forward_validation_codes():
     for n, _ in binding.ForwardArgs._fields_:
         if n not in ("struct_size", "dtype", "num_tokens", "hidden", "inter", "num_experts",
                      "top_k", "num_loras", "max_rank", "block_m", "workspace_bytes",
-                     "out_dtype"):
+                     "out_dtype", "weight_dtype"):
             setattr(bare, n, None)
     assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(bare)) == ws
     assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(dtype=9))) == 0
     assert call(num_tokens=0) == binding.OK
+
+
+def test_forward_fp8_weight_validation():
+    lib = binding.lib()
+    call = lambda **o: lib.moe_lora_forward(ctypes.byref(_fargs(**o)), None)  # noqa: E731
+    F8 = binding.DTYPE_FP8_E4M3
+    # H = 128, I = 256: valid fp8 shapes (the 1-byte workspace is the only error)
+    assert call(weight_dtype=F8) == binding.ERR_WORKSPACE
+    assert call(weight_dtype=binding.DTYPE_BF16) == binding.ERR_WORKSPACE   # same as dtype
+    assert call(weight_dtype=F8, dtype=binding.DTYPE_F32, out_dtype=binding.DTYPE_F32) == \
+        binding.ERR_UNSUPPORTED                                             # fp8 needs bf16 x
+    assert call(weight_dtype=F8, hidden=192) == binding.ERR_UNSUPPORTED     # H % 128
+    assert call(weight_dtype=F8, inter=320) == binding.ERR_UNSUPPORTED      # I % 128
+    assert call(weight_dtype=F8, hidden=16384 + 128) == binding.ERR_UNSUPPORTED
+    assert call(weight_dtype=3) == binding.ERR_UNSUPPORTED
+    assert call(weight_dtype=F8, w_down_scale=None) == binding.ERR_INVALID
+    assert call(weight_dtype=F8, w_gate_up_scale=None) == binding.ERR_INVALID
+    assert call(weight_dtype=F8, w_gate_up_scale=None, num_tokens=0) == binding.OK
+    # a caller whose struct ends at out_dtype gets weights in dtype
+    old = binding.ForwardArgs.out_dtype.offset + 4          # the struct before the fp8 fields
+    assert call(struct_size=old, weight_dtype=3) == binding.ERR_WORKSPACE
+    assert call(struct_size=old + 4, weight_dtype=3) == binding.ERR_WORKSPACE   # with its padding
+    assert call(struct_size=old - 4) == binding.ERR_INVALID
+    ws8 = lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(weight_dtype=F8)))
+    assert ws8 == lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
 
 
 def test_binding_refuses_host_tensors():

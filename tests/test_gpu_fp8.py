@@ -1,0 +1,74 @@
+"""GPU parity of the layer with fp8 expert weights (OCP e4m3 codes, 128 x 128
+block scales; x, LoRA pools and y in bf16) against the oracle, which decodes
+the codes from the format's definition and dequantizes in float64.
+
+The bar is the bf16 layer bar: the kernels convert each code exactly and round
+code * scale to bf16 before the matrix cores, an error of at most half a bf16
+ulp per weight, of the same order as the bf16 rounding of the activations."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_layer_close, gpu_inputs, oracle_forward, run, say, to_np
+from moe_expert_layer_segment_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, E, k, H, I, L, ranks, seg_lens, weight_indices, R
+    ("fp8_tiles", 8, 2, 256, 384, 4, [0, 8, 16, 16], [40, 1, 77, 3, 90, 29], [2, 0, 3, 2, -1, 1], 16),
+    ("fp8_ragged_down_cols", 6, 3, 384, 256, 3, [32, 12, 5], [33, 64, 7], [0, 1, 2], 32),
+    ("fp8_rank64_long_k", 16, 4, 1024, 512, 5, [64, 0, 8, 64, 33], [100, 50, 150, 10], [0, 4, 3, -1], 64),
+    ("fp8_one_token", 4, 1, 128, 128, 2, [8, 8], [1], [1], 8),
+]
+
+
+def _y32(inp, **kw):
+    y32 = run(inp, out_dtype=torch.float32, **kw)
+    y16 = run(inp, **kw)
+    assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 y is not the rounded fp32 y"
+    return to_np(y32)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_fp8_small_full(case):
+    name, E, k, H, I, L, ranks, lens, wi, R = case
+    say(f"forward fp8 small {name}")
+    spec = workloads.LayerSpec(name, E, k, H, I, L, ranks, lens, wi, seed=19, pool_rank=R,
+                               weights="fp8")
+    inp = gpu_inputs(spec)
+    assert inp["w_gate_up"].dtype == torch.uint8
+    assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", name)
+
+
+def test_fp8_base_only():
+    spec = workloads.LayerSpec("fp8_base", 8, 2, 256, 256, 2, [16, 16], [20, 30], [0, 1],
+                               seed=20, pool_rank=16, weights="fp8")
+    say("forward fp8 without LoRA")
+    inp = gpu_inputs(spec, with_lora=False)
+    got = to_np(run(inp, with_lora=False, out_dtype=torch.float32))
+    assert_layer_close(got, oracle_forward(inp, with_lora=False), "bf16", "fp8 base")
+
+
+def test_fp8_down_k_split():
+    spec = workloads.LayerSpec("fp8_down_k_split", 4, 2, 128, 8192, 2, [16, 8], [30, 1, 25, 8],
+                               [0, -1, 1, 0], seed=28, pool_rank=16, weights="fp8")
+    say("forward fp8 with the down GEMM's K split (I = 8192)")
+    inp = gpu_inputs(spec)
+    assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", "fp8 down K split")
+
+
+@pytest.mark.parametrize("name,n_sample", [("c1_fp8", 40), ("c3_fp8", 40), ("c4d_fp8", 16),
+                                           ("c4p_fp8", 12)])
+def test_fp8_full_size_sampled(name, n_sample):
+    spec = workloads.config(name)
+    say(f"forward full-size {name}: T={spec.num_tokens}")
+    inp = gpu_inputs(spec)
+    got = to_np(run(inp, out_dtype=torch.float32))
+    assert np.all(np.isfinite(got))
+    T = spec.num_tokens
+    sample = np.unique(np.concatenate([np.linspace(0, T - 1, n_sample).astype(np.int64), [0, T - 1]]))
+    ref = oracle_forward(inp, tokens=sample)
+    assert_layer_close(got[sample], ref, "bf16", f"{name} ({len(sample)} sampled tokens)")
+    del inp
+    torch.cuda.empty_cache()

@@ -36,6 +36,10 @@ MUTANTS = {
                         "order = np.lexsort((expert, lg[t]))[:top_k]"),
     "route_no_renorm": ("w[t] = e / e.sum()", "w[t] = e"),
     "route_softmax_over_all": ("w[t] = e / e.sum()", "w[t] = e / np.exp(lg[t] - top[0]).sum()"),
+    "e4m3_bias_8": ("np.exp2(exp.astype(np.float64) - 7.0)", "np.exp2(exp.astype(np.float64) - 8.0)"),
+    "e4m3_subnormal_scale": ("subnormal = man * 2.0 ** -9", "subnormal = man * 2.0 ** -10"),
+    "e4m3_no_nan": ("return np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, v)", "return v"),
+    "dequant_scale_dropped": ("    return w * s_full", "    return w"),
     "brute_b_untransposed": ("Bd = _f64(b_down[l, e])[:r].T      # [H, r]", "Bd = _f64(b_down[l, e])[:r].T[::-1]"),
 }
 
