@@ -495,10 +495,24 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t
 // 16 fp8 e4m3 codes (4 dwords, element 4w+b = byte b of dword w) times a
 // block scale, as two bf16x8 fragments: elements 0..7 and 8..15.  The code
 // itself converts exactly (every e4m3 value is a bf16 value); the product
-// with the scale is rounded to nearest-even bf16 (exact for a power-of-two
-// scale).
-__device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bf16x8& lo, bf16x8& hi) {
+// with the scale is rounded to nearest-even bf16.  A positive normal
+// power-of-two scale (pow2, wave-uniform) makes the product exact: then the
+// scaled conversion instruction, which applies only the scale's exponent,
+// gives the same bits at one instruction per two codes.
+__device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bool pow2, bf16x8& lo, bf16x8& hi) {
   typedef float float2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  if (pow2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[w], sc, false);
+      const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[w], sc, true);
+      bf16x8& d = w < 2 ? lo : hi;
+      const int o = 4 * (w & 1);
+      d[o + 0] = p0[0]; d[o + 1] = p0[1]; d[o + 2] = p1[0]; d[o + 3] = p1[1];
+    }
+    return;
+  }
   float f[16];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -535,10 +549,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   constexpr int BK = ROWB / sizeof(T);            // K elements per tile
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
   constexpr int RPS = 1024 / ROWB;                // rows per 1 KB DMA segment
-  static_assert(ROWB == 64 || ROWB == 128, "row size");
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row size");
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr bool WF8 = sizeof(W) == 1;            // fp8 weights: B rows hold BK one-byte codes
-  static_assert(!WF8 || (sizeof(T) == 2 && ROWB == 128), "fp8 weights with bf16 activations");
+  static_assert(!WF8 || (sizeof(T) == 2 && ROWB >= 128), "fp8 weights with bf16 activations");
   constexpr int ROWB_B = WF8 ? ROWB / 2 : ROWB;   // bytes per LDS row of B
   constexpr int CPR_B = ROWB_B / 16, RPS_B = 1024 / ROWB_B;
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB_B;
@@ -639,10 +653,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // (l%8) ^ swz(row).  Rows outside the tile (pads, rows past nrows, columns
   // past n_out) load a valid row instead: MFMA rows / columns are
   // independent and those results are never stored.
-  // 16 lanes read 16 consecutive rows at one chunk: with 128-byte rows, rows
-  // 2 apart share banks, with 64-byte rows rows 4 apart
+  // 16 lanes read 16 consecutive rows at one chunk: with 256-byte rows every
+  // row starts at the same bank, with 128-byte rows rows 2 apart share banks,
+  // with 64-byte rows rows 4 apart
   auto swz = [](int row) -> int {
-    return ROWB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+    return ROWB == 256 ? (row & 15) : ROWB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
   };
   // B rows: 64-byte rows (fp8) swizzle like 64-byte A rows would
   auto swzb = [](int n) -> int {
@@ -802,6 +817,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // holds the converted fragments; sck[j] the K tile's block scales.
   frag fbq[2][2][NB];
   float sck[NB];
+  bool sc_pow2[NB];
   auto load_frags = [&](const char* base, int ks, int set) {
     const int kel = WF8 ? 32 * (ks >> 1) + 2 * lk + 8 * (ks & 1) : ks * KF + lk;
 #pragma unroll
@@ -816,7 +832,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
         for (int j = 0; j < NB; ++j) {
           const int n = b_row_of(j) - BM;
           const int4v raw = *reinterpret_cast<const int4v*>(base + A_BYTES + n * ROWB_B + ((kc ^ swzb(n)) * 16));
-          fp8x16_to_bf16(raw, sck[j], fbq[(ks >> 1) & 1][0][j], fbq[(ks >> 1) & 1][1][j]);
+          fp8x16_to_bf16(raw, sck[j], sc_pow2[j], fbq[(ks >> 1) & 1][0][j], fbq[(ks >> 1) & 1][1][j]);
         }
       }
     }
@@ -852,7 +868,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       const char* base = lds + buf * STAGE_BYTES;
       if constexpr (WF8) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) sck[j] = sc_lds[(wave * NB + j) * MAXKB + (kt * BK) / 128];
+        for (int j = 0; j < NB; ++j) {
+          // one scale per wave (its columns share a 128-row block): a scalar
+          const uint32_t bits = __builtin_amdgcn_readfirstlane(
+              __builtin_bit_cast(uint32_t, sc_lds[(wave * NB + j) * MAXKB + (kt * BK) / 128]));
+          sck[j] = __builtin_bit_cast(float, bits);
+          const uint32_t ex = (bits >> 23) & 0xFF;
+          sc_pow2[j] = (bits & 0x807FFFFFu) == 0 && ex != 0 && ex != 0xFF;
+        }
       }
       load_frags(base, 0, 0);
       static_for<KSUB>([&](auto KS) {
@@ -1121,14 +1144,24 @@ template <> struct TileCfg<bf16_t> {
                        ROWB = MOELORA_BF16_ROWB, PER_CU = 1;
   static constexpr int BN_DOWN = MOELORA_BF16_BN_DOWN, STAGES_DOWN = MOELORA_BF16_STAGES_DOWN;
 };
-// fp8 e4m3 weights (bf16 activations): the same tile; the B half of a stage
-// is half as large (32 KB stages), so the ring is 4 deep (128 KB, which also
-// holds the down epilogue's fp32 staging)
+// fp8 e4m3 weights (bf16 activations), the same 128 x 256 tile.  Batches
+// with many pairs per expert (prefill) take 128-deep K tiles, so a weight row
+// is fetched 128 bytes at a time (256-byte x rows), in two 64 KB stages;
+// decode-sized batches take 64-deep K tiles in a 4-deep ring of 32 KB stages,
+// which starts each short tile sooner.  Either ring is 128 KB, which also
+// holds the down epilogue's fp32 staging.
 struct Fp8Cfg {
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 2, ROWB = 256, PER_CU = 1;
+};
+struct Fp8DecodeCfg {
   static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 4, ROWB = 128, PER_CU = 1;
 };
+#ifndef MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT
+#define MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT 64
+#endif
 static_assert(Fp8Cfg::BM == TileCfg<bf16_t>::BM && Fp8Cfg::BN == TileCfg<bf16_t>::BN &&
-                  Fp8Cfg::BN == TileCfg<bf16_t>::BN_DOWN,
+                  Fp8Cfg::BN == TileCfg<bf16_t>::BN_DOWN && Fp8DecodeCfg::BM == Fp8Cfg::BM &&
+                  Fp8DecodeCfg::BN == Fp8Cfg::BN,
               "fp8 tiles share the work items and column tiles of the bf16 path");
 template <> struct TileCfg<float> {
   static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, ROWB = 128, PER_CU = 2;
@@ -1249,6 +1282,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN;
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   const bool fp8w = kBf16 && p.wdtype == kWeightFp8;
+  const bool fp8_deep_k = P >= (int64_t)MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT * p.E;
 
   mark(2 * kStagePlan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, (int)p.E, (int)p.BM, BM,
@@ -1321,8 +1355,12 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageGateUp);
     if constexpr (kBf16) {
-      if (fp8w) {
+      if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
+        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+      } else if (fp8w) {
+        typedef Fp8DecodeCfg F;
         hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
       }
@@ -1382,8 +1420,12 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     mark(2 * kStageDown);
     if constexpr (kBf16) {
-      if (fp8w) {
+      if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
+        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+      } else if (fp8w) {
+        typedef Fp8DecodeCfg F;
         hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
       }

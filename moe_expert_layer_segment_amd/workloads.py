@@ -22,10 +22,11 @@ silent:
   stored as float32.
 * Each tensor (and each expert slice of it) has its own sub-seed derived from
   ``(seed, tensor_id, expert)``, so any expert can be regenerated on its own.
-* fp8 expert weights (``weights="fp8"``): each expert's fp32 draw is quantized
-  to OCP e4m3 codes over 128 x 128 blocks with scale = block amax / 448 (the
-  largest finite e4m3 value), the usual block-scaled recipe; x, pools and y
-  stay bf16.
+* fp8 expert weights: each expert's fp32 draw is quantized to OCP e4m3 codes
+  over 128 x 128 blocks; x, pools and y stay bf16.  ``weights="fp8"`` uses
+  power-of-two block scales, 2^ceil(log2(amax / 448)) (448 = the largest finite
+  e4m3 value; the UE8M0 scale recipe); ``weights="fp8_f32scale"`` uses
+  scale = amax / 448 exactly.
 """
 from __future__ import annotations
 
@@ -58,7 +59,7 @@ class LayerSpec:
     router: str = "normal"       # "normal" | "zipf" | "uniform_bias"
     alpha_over_rank: float = 2.0  # scaling = alpha / r with alpha = 2r
     pool_rank: Optional[int] = None
-    weights: str = "same"        # "same" (dtype) or "fp8": e4m3 codes + 128 x 128 block scales
+    weights: str = "same"        # "same" (dtype), "fp8" / "fp8_f32scale": e4m3 codes + 128 x 128 block scales
 
     @property
     def num_tokens(self) -> int:
@@ -210,15 +211,18 @@ def route(logits: np.ndarray, k: int):
 # ----------------------------------------------------------------------------
 # tensors
 # ----------------------------------------------------------------------------
-def quantize_fp8_blocks(w: torch.Tensor, block: int = 128):
+def quantize_fp8_blocks(w: torch.Tensor, block: int = 128, pow2: bool = False):
     """Input preparation for fp8 weights: a float [N, K] matrix as (OCP e4m3
     codes uint8 [N, K], float32 scales [N / block, K / block]) with
-    scale = block amax / 448 (1 for an all-zero block) and code = the e4m3
-    rounding of w / scale."""
+    scale = block amax / 448, or the next power of two up from it when
+    ``pow2`` (1 for an all-zero block), and code = the e4m3 rounding of
+    w / scale."""
     N, K = w.shape
     b = w.float().reshape(N // block, block, K // block, block)
     amax = b.abs().amax(dim=(1, 3))
     scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    if pow2:
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
     q = (b / scale[:, None, :, None]).reshape(N, K).to(torch.float8_e4m3fn)
     return q.view(torch.uint8), scale
 
@@ -257,7 +261,8 @@ def generate(spec: LayerSpec, device="cpu", canary: bool = True,
     out: Dict[str, object] = {}
     x_key = 0 if not spec.name.startswith("c4d") else 1
     out["x"] = _randn((T, H), 1.0, _subseed(s, _TID_X, x_key), dev, dt)
-    if spec.weights == "fp8":
+    if spec.weights in ("fp8", "fp8_f32scale"):
+        pow2 = spec.weights == "fp8"
         if dt != torch.bfloat16:
             raise ValueError("fp8 expert weights go with bf16 activations")
         wgu = torch.empty((E, 2 * I, H), device=dev, dtype=torch.uint8)
@@ -266,9 +271,11 @@ def generate(spec: LayerSpec, device="cpu", canary: bool = True,
         sd = torch.empty((E, H // 128, I // 128), device=dev, dtype=torch.float32)
         for e in range(E):
             wgu[e], sgu[e] = quantize_fp8_blocks(
-                _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, torch.float32))
+                _randn((2 * I, H), 1.0 / np.sqrt(H), _subseed(s, _TID_WGU, e), dev, torch.float32),
+                pow2=pow2)
             wd[e], sd[e] = quantize_fp8_blocks(
-                _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, torch.float32))
+                _randn((H, I), 1.0 / np.sqrt(I), _subseed(s, _TID_WD, e), dev, torch.float32),
+                pow2=pow2)
         out["w_gate_up_scale"], out["w_down_scale"] = sgu, sd
     else:
         wgu = torch.empty((E, 2 * I, H), device=dev, dtype=dt)

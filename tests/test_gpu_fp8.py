@@ -1,5 +1,5 @@
 """GPU parity of the layer with fp8 expert weights (OCP e4m3 codes, 128 x 128
-block scales; x, LoRA pools and y in bf16) against the oracle, which decodes
+block scales, power-of-two or general fp32; x, LoRA pools and y in bf16) against the oracle, which decodes
 the codes from the format's definition and dequantizes in float64.
 
 The bar is the bf16 layer bar: the kernels convert each code exactly and round
@@ -20,6 +20,8 @@ SMALL = [
     ("fp8_ragged_down_cols", 6, 3, 384, 256, 3, [32, 12, 5], [33, 64, 7], [0, 1, 2], 32),
     ("fp8_rank64_long_k", 16, 4, 1024, 512, 5, [64, 0, 8, 64, 33], [100, 50, 150, 10], [0, 4, 3, -1], 64),
     ("fp8_one_token", 4, 1, 128, 128, 2, [8, 8], [1], [1], 8),
+    # >= 64 pairs per expert: the 128-deep K tiles of prefill-sized batches
+    ("fp8_deep_k", 2, 2, 512, 384, 3, [16, 0, 32], [70, 50, 80], [0, 1, 2], 32),
 ]
 
 
@@ -30,15 +32,20 @@ def _y32(inp, **kw):
     return to_np(y32)
 
 
+@pytest.mark.parametrize("scales", ["fp8", "fp8_f32scale"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_fp8_small_full(case):
+def test_fp8_small_full(case, scales):
+    # power-of-two block scales take the scaled conversion instruction, other
+    # fp32 scales the exact multiply; both round code * scale to bf16
     name, E, k, H, I, L, ranks, lens, wi, R = case
-    say(f"forward fp8 small {name}")
+    say(f"forward fp8 small {name} ({scales})")
     spec = workloads.LayerSpec(name, E, k, H, I, L, ranks, lens, wi, seed=19, pool_rank=R,
-                               weights="fp8")
+                               weights=scales)
     inp = gpu_inputs(spec)
     assert inp["w_gate_up"].dtype == torch.uint8
-    assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", name)
+    sc = inp["w_gate_up_scale"]
+    assert bool(torch.all(torch.exp2(torch.round(torch.log2(sc))) == sc)) == (scales == "fp8")
+    assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", f"{name} {scales}")
 
 
 def test_fp8_base_only():
@@ -50,10 +57,12 @@ def test_fp8_base_only():
     assert_layer_close(got, oracle_forward(inp, with_lora=False), "bf16", "fp8 base")
 
 
-def test_fp8_down_k_split():
-    spec = workloads.LayerSpec("fp8_down_k_split", 4, 2, 128, 8192, 2, [16, 8], [30, 1, 25, 8],
-                               [0, -1, 1, 0], seed=28, pool_rank=16, weights="fp8")
-    say("forward fp8 with the down GEMM's K split (I = 8192)")
+@pytest.mark.parametrize("E,lens", [(4, [30, 1, 25, 8]), (2, [70, 50, 80])],
+                         ids=["decode_tiles", "deep_k_tiles"])
+def test_fp8_down_k_split(E, lens):
+    spec = workloads.LayerSpec("fp8_down_k_split", E, 2, 128, 8192, 2, [16, 8], lens,
+                               [0, -1, 1, 0][:len(lens)], seed=28, pool_rank=16, weights="fp8")
+    say(f"forward fp8 with the down GEMM's K split (I = 8192, E = {E})")
     inp = gpu_inputs(spec)
     assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", "fp8 down K split")
 
