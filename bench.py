@@ -275,6 +275,119 @@ def cpu_baseline(spec, inp, n_tokens, min_seconds):
                        f"touched weights; {dt:.1f} s")
 
 
+def dense_main(args, torch, binding, workloads, dev):
+    """The second workload: the dense two-slice LoRA projection (info + align +
+    dense forward per step), one JSON line in the same shape as the layer's."""
+    spec = workloads.dense_config(args.config)
+    print(f"[bench] generating {spec.name} on {dev}", file=sys.stderr, flush=True)
+    inp = workloads.generate_dense(spec, device=dev, canary=False)
+    T, H, N0, N1, L = spec.num_tokens, spec.hidden, spec.out0, spec.out1, spec.num_loras
+    N = N0 + N1
+    BM = 16
+    pools = {n: inp[n] for n in ("a0", "a1", "b0", "b1")} if L > 0 else None
+    en_buf = torch.empty(max(L, 1), dtype=torch.int32, device=dev)
+    mp_buf = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    en, mp = binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
+                                   en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+    al = binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, 1, L, BM)
+    al_ws = torch.empty(binding.moe_lora_align_workspace_bytes(T, 1, 1, L, BM), dtype=torch.uint8,
+                        device=dev)
+    y = torch.empty((T, N), dtype=inp["x"].dtype, device=dev)
+    ws = torch.empty(binding.moe_lora_dense_workspace_bytes(
+        inp["x"], inp["w"], N0, al, inp["lora_ranks"], inp["scaling"], pools), dtype=torch.uint8,
+        device=dev)
+    hip = HipEvents()
+    nst = len(binding.DENSE_STAGES)
+
+    def step(events=None):
+        binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
+                              en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+        binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, 1, L, BM, out=al,
+                               workspace=al_ws)
+        binding.moe_lora_dense_forward(inp["x"], inp["w"], N0, al,
+                                       inp["lora_ranks"] if L > 0 else None,
+                                       inp["scaling"] if L > 0 else None, pools, y=y,
+                                       workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [hip.create(2 * nst) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for st in range(args.steps):
+        step(ev[st])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in ev]))
+                for i, name in enumerate(binding.DENSE_STAGES)}
+    for e in ev:
+        hip.destroy(e)
+
+    m = inp["meta"]
+    ranks = np.asarray(m["lora_ranks"])
+    tok_slot = np.repeat(np.asarray(m["weight_indices"]), np.diff(np.asarray(m["seg_indptr"])))
+    used = set(int(v) for v in tok_slot if v >= 0)
+    r_tok = np.array([ranks[l] if (l >= 0 and l in used and ranks[l] > 0) else 0 for l in tok_slot])
+    esz = 2 if spec.dtype == "bf16" else 4
+    gemm_flops = 2.0 * T * H * N + 2.0 * float(np.sum(r_tok)) * N
+    total_flops = gemm_flops + 2.0 * float(np.sum(r_tok)) * H * (2 if N1 > 0 else 1)
+    gemm_bytes = N * H * esz + T * H * esz + 4.0 * T * N
+    g_ms = stage_ms["gemm"]
+    peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_FP32_TFLOPS
+    if gemm_flops / gemm_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        a = gemm_flops / (g_ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(a, 2), peak=peak, unit="TFLOP/s",
+                        frac=round(a / peak, 4), traffic=None, kernel="dense_gemm",
+                        kernel_ms=round(g_ms, 4), kernel_flops=gemm_flops)
+    else:
+        gbs = gemm_bytes / (g_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None, kernel="dense_gemm",
+                        kernel_ms=round(g_ms, 4), kernel_bytes=gemm_bytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = T if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, T)
+        sample = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
+        xh = inp["x"].float().cpu().numpy()
+        wh = inp["w"].float().cpu().numpy()
+        ph = {k: v.float().cpu().numpy() for k, v in (pools or {}).items()}
+        t0, passes = time.perf_counter(), 0
+        while passes < 8 and (passes == 0 or time.perf_counter() - t0 < args.cpu_min_seconds):
+            en_o, mp_o = oracle.moe_lora_info(T, m["seg_indptr"], m["weight_indices"],
+                                              m["lora_ranks"], m["max_seg_len"])
+            oracle.dense_lora_forward(xh, wh, N0, m["lora_ranks"], m["scaling"], mp_o, en_o,
+                                      tokens=sample, **ph)
+            passes += 1
+        dt = time.perf_counter() - t0
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        omp = os.environ.get("OMP_NUM_THREADS")
+        if omp and omp.isdigit():
+            cores = min(cores, int(omp))
+        cpu = dict(value=passes * len(sample) / dt, unit="tokens/s", cores=cores, kind="oracle",
+                   sample=f"{len(sample)} of {T} tokens (evenly spaced), {passes} pass(es); "
+                          f"float64 numpy oracle; {dt:.1f} s")
+    out = {
+        "metric": "dense LoRA projection tokens/s", "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "hidden": H, "out0": N0, "out1": N1, "tokens": T,
+                   "requests": spec.num_reqs, "adapter_slots": L, "lora_ranks": list(spec.lora_ranks),
+                   "block_m": BM, "parallelism": "tp1"},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -295,6 +408,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config in workloads.DENSE_CONFIG_NAMES:
+        dense_main(args, torch, binding, workloads, dev)
+        return
     spec = workloads.config(args.config)
     print(f"[bench] generating {spec.name} on {dev}", file=sys.stderr, flush=True)
     inp = workloads.generate(spec, device=dev, canary=False)

@@ -259,6 +259,66 @@ int moe_lora_forward(const moe_lora_forward_args* args, void* stream);
 int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
                             void* const* events);
 
+/*
+ * Dense projection with per-request LoRA and a two-slice output ("LoRA on a
+ * fused projection whose outputs have unequal sizes": the SGLang PR #22323
+ * page, sections 功能与动机 and 实现拆解 item 2 -- the fused q_a_proj +
+ * kv_a_proj_with_mqa projection of MLA, whose LoRA B is split in two and
+ * applied per output part).  For token t in a request using slot l:
+ *
+ *   y[t, 0:N0)        = x_t W[0:N0)^T     + on * s_l (x_t A0_l^T) B0_l^T
+ *   y[t, N0:N0+N1)    = x_t W[N0:N0+N1)^T + on * s_l (x_t A1_l^T) B1_l^T
+ *
+ * with on = (l >= 0 && adapter_enabled[l] && lora_ranks[l] > 0), exactly the
+ * masking of the MoE layer.  The batch metadata comes from moe_lora_info and
+ * moe_lora_align called with num_experts = 1, top_k = 1 and topk_ids all 0
+ * (align then buckets the tokens by slot).
+ *
+ *   x            [T, H]            activations (dtype).
+ *   w            [N0 + N1, H]      the fused weight, rows [0, N0) slice 0.
+ *   a0, a1       [L, R, H]         LoRA A of slice 0 / 1, rank-major.
+ *   b0           [L, R, N0]        LoRA B of slice 0, stored transposed.
+ *   b1           [L, R, N1]        LoRA B of slice 1 (a1, b1 may be NULL when N1 == 0).
+ *   lora_ranks   [L] int32, scaling [L] float32: as for the MoE layer.
+ *   the align outputs, workspace (>= moe_lora_dense_workspace_bytes) and
+ *   y            [T, N0 + N1] out  overwritten, in out_dtype (dtype or F32).
+ * H, N0 and N1 must be multiples of 64 (N0 > 0, N1 >= 0), R <= 64.  Errors and
+ * ownership as for moe_lora_forward.
+ */
+typedef struct moe_lora_dense_args {
+  size_t struct_size; /* sizeof(moe_lora_dense_args) */
+  int32_t dtype;      /* MOE_LORA_F32 or MOE_LORA_BF16 */
+  int32_t num_tokens, hidden, out0, out1, num_loras, max_rank, block_m;
+  const void* x;
+  const void* w;
+  const void* a0;
+  const void* a1;
+  const void* b0;
+  const void* b1;
+  const int32_t* lora_ranks;
+  const float* scaling;
+  const int32_t* sorted_pair_ids;
+  const int32_t* tile_expert;
+  const int32_t* tile_lora;
+  const int32_t* expert_tile_offsets;
+  const int32_t* num_rows_padded;
+  void* workspace;
+  size_t workspace_bytes;
+  void* y;
+  int32_t out_dtype;
+} moe_lora_dense_args;
+
+/* Workspace bytes moe_lora_dense_forward needs for the sizes in `args` (0 if invalid). */
+size_t moe_lora_dense_workspace_bytes(const moe_lora_dense_args* args);
+
+int moe_lora_dense_forward(const moe_lora_dense_args* args, void* stream);
+
+/* moe_lora_dense_forward plus caller-owned HIP events recorded around its four
+ * kernel stages (plan, shrink, GEMM, combine): events[2s] before and
+ * events[2s+1] after stage s; NULL entries are skipped.  Measurement only. */
+int moe_lora_dense_forward_events(const moe_lora_dense_args* args, void* stream,
+                                  void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

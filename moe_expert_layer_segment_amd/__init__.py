@@ -9,9 +9,12 @@ from .binding import (  # noqa: F401
     moe_lora_align,
     moe_lora_align_capacity_rows,
     moe_lora_align_workspace_bytes,
+    moe_lora_dense_forward,
+    moe_lora_dense_workspace_bytes,
     moe_lora_forward,
     moe_lora_forward_workspace_bytes,
     moe_lora_info,
     moe_lora_route,
+    run_dense,
     run_layer,
 )

@@ -379,3 +379,140 @@ def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True,
                             inputs["w_down"], al, k, ranks if L > 0 else None,
                             inputs["scaling"] if L > 0 else None, pools, out_dtype=out_dtype,
                             w_scales=ws)
+
+
+# ---------------------------------------------------------------------------
+# dense projection with a two-slice LoRA output
+# ---------------------------------------------------------------------------
+DENSE_STAGES = ("plan", "shrink", "gemm", "combine")
+
+
+class DenseArgs(ctypes.Structure):
+    """Mirror of ``moe_lora_dense_args``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("dtype", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("out0", ctypes.c_int32),
+        ("out1", ctypes.c_int32), ("num_loras", ctypes.c_int32), ("max_rank", ctypes.c_int32),
+        ("block_m", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("w", ctypes.c_void_p),
+        ("a0", ctypes.c_void_p), ("a1", ctypes.c_void_p), ("b0", ctypes.c_void_p),
+        ("b1", ctypes.c_void_p),
+        ("lora_ranks", ctypes.c_void_p), ("scaling", ctypes.c_void_p),
+        ("sorted_pair_ids", ctypes.c_void_p), ("tile_expert", ctypes.c_void_p),
+        ("tile_lora", ctypes.c_void_p), ("expert_tile_offsets", ctypes.c_void_p),
+        ("num_rows_padded", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("y", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+    ]
+
+
+def _dense_args(x, w, out0, align_out, lora_ranks, scaling, pools, y, workspace,
+                out_dtype=None) -> DenseArgs:
+    T, H = x.shape
+    N, H2 = w.shape
+    if H2 != H or not (0 < out0 <= N):
+        raise ValueError("w must be [out0 + out1, H] with 0 < out0 <= its rows")
+    if x.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    dev = x.device
+    _need(x, "x", x.dtype)
+    _need(w, "w", x.dtype, dev)
+    out1 = N - out0
+    L, R = 0, 0
+    if pools is not None:
+        L, R, _ = pools["a0"].shape
+        shapes = dict(a0=(L, R, H), a1=(L, R, H), b0=(L, R, out0), b1=(L, R, out1))
+        for n in ("a0", "b0") + (("a1", "b1") if out1 > 0 else ()):
+            _need(pools[n], n, x.dtype, dev)
+            if tuple(pools[n].shape) != shapes[n]:
+                raise ValueError(f"{n} must have shape {shapes[n]}, got {tuple(pools[n].shape)}")
+        _need(lora_ranks, "lora_ranks", torch.int32, dev, L)
+        _need(scaling, "scaling", torch.float32, dev, L)
+    a = DenseArgs()
+    a.struct_size = ctypes.sizeof(DenseArgs)
+    a.dtype = dt
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    if out_dt == torch.float32:
+        a.out_dtype = DTYPE_F32
+    elif out_dt == x.dtype:
+        a.out_dtype = dt
+    else:
+        raise TypeError(f"unsupported output dtype {out_dt}")
+    a.num_tokens, a.hidden, a.out0, a.out1 = T, H, out0, out1
+    a.num_loras, a.max_rank, a.block_m = L, R, int(align_out["block_m"])
+    a.x, a.w = x.data_ptr(), w.data_ptr()
+    if pools is not None:
+        a.a0, a.b0 = pools["a0"].data_ptr(), pools["b0"].data_ptr()
+        if out1 > 0:
+            a.a1, a.b1 = pools["a1"].data_ptr(), pools["b1"].data_ptr()
+        a.lora_ranks, a.scaling = lora_ranks.data_ptr(), scaling.data_ptr()
+    for n in ("sorted_pair_ids", "tile_expert", "tile_lora", "expert_tile_offsets",
+              "num_rows_padded"):
+        _need(align_out[n], n, torch.int32, dev)
+        setattr(a, n, align_out[n].data_ptr())
+    if y is not None:
+        _need(y, "y", out_dt, dev, T * N)
+        a.y = y.data_ptr()
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return a
+
+
+def moe_lora_dense_workspace_bytes(x, w, out0, align_out, lora_ranks=None, scaling=None,
+                                   pools=None) -> int:
+    a = _dense_args(x, w, out0, align_out, lora_ranks, scaling, pools, None, None)
+    n = int(lib().moe_lora_dense_workspace_bytes(ctypes.byref(a)))
+    if n == 0:
+        raise MoeLoraError(ERR_INVALID, "moe_lora_dense_workspace_bytes")
+    return n
+
+
+def moe_lora_dense_forward(x: torch.Tensor, w: torch.Tensor, out0: int,
+                           align_out: Dict[str, torch.Tensor],
+                           lora_ranks: Optional[torch.Tensor] = None,
+                           scaling: Optional[torch.Tensor] = None,
+                           pools: Optional[Dict[str, torch.Tensor]] = None,
+                           y: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           events=None, out_dtype=None) -> torch.Tensor:
+    """Dense projection with per-request LoRA and two output slices: y [T, N]
+    (``pools``: a0, a1 [L, R, H], b0 [L, R, out0], b1 [L, R, N - out0]).
+    ``align_out`` comes from moe_lora_align with one expert and top_k = 1."""
+    T = x.shape[0]
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((T, N), dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    if workspace is None:
+        n = moe_lora_dense_workspace_bytes(x, w, out0, align_out, lora_ranks, scaling, pools)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    a = _dense_args(x, w, out0, align_out, lora_ranks, scaling, pools, y, workspace, out_dtype)
+    if events is None:
+        _check(lib().moe_lora_dense_forward(ctypes.byref(a), _stream()), "moe_lora_dense_forward")
+    else:
+        if len(events) != 2 * len(DENSE_STAGES):
+            raise ValueError("events needs one pair per dense stage")
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().moe_lora_dense_forward_events(ctypes.byref(a), _stream(), arr),
+               "moe_lora_dense_forward_events")
+    return y
+
+
+def run_dense(inputs: dict, out0: int, block_m: int = 16, with_lora: bool = True,
+              out_dtype=None) -> torch.Tensor:
+    """info -> align (one expert, top_k = 1) -> dense forward on a dict from
+    ``workloads.generate_dense``."""
+    T = inputs["x"].shape[0]
+    L = inputs["lora_ranks"].numel() if with_lora and "a0" in inputs else 0
+    ranks = inputs["lora_ranks"]
+    en, mp = moe_lora_info(T, inputs["seg_indptr"], ranks, inputs["weight_indices"],
+                           max_len=inputs["meta"]["max_seg_len"])
+    al = moe_lora_align(inputs["topk_ids"], mp, en if L > 0 else None, 1, L, block_m)
+    pools = {n: inputs[n] for n in ("a0", "a1", "b0", "b1")} if L > 0 else None
+    return moe_lora_dense_forward(inputs["x"], inputs["w"], out0, al, ranks if L > 0 else None,
+                                  inputs["scaling"] if L > 0 else None, pools,
+                                  out_dtype=out_dtype)

@@ -178,4 +178,65 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
   return forward_impl(args, stream, events);
 }
 
+static int to_dense(const moe_lora_dense_args* a, DenseProblem* p, bool check_ptrs) {
+  if (!a || a->struct_size < sizeof(moe_lora_dense_args)) return MOE_LORA_ERR_INVALID;
+  if (a->dtype != MOE_LORA_F32 && a->dtype != MOE_LORA_BF16) return MOE_LORA_ERR_UNSUPPORTED;
+  if (a->num_tokens < 0 || a->hidden <= 0 || a->out0 <= 0 || a->out1 < 0 || a->num_loras < 0 ||
+      a->max_rank < 0 || bad_block_m(a->block_m))
+    return MOE_LORA_ERR_INVALID;
+  if (a->hidden % 64 || a->out0 % 64 || a->out1 % 64) return MOE_LORA_ERR_UNSUPPORTED;
+  if (a->max_rank > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
+  if (a->num_loras > 0 && a->max_rank <= 0) return MOE_LORA_ERR_INVALID;
+  if ((int64_t)a->num_loras + 1 > kMaxKeys) return MOE_LORA_ERR_UNSUPPORTED;
+  if (a->out_dtype != a->dtype && a->out_dtype != MOE_LORA_F32) return MOE_LORA_ERR_UNSUPPORTED;
+  if (check_ptrs && a->num_tokens > 0) {
+    if (!a->x || !a->w || !a->sorted_pair_ids || !a->tile_expert || !a->tile_lora ||
+        !a->expert_tile_offsets || !a->num_rows_padded || !a->y)
+      return MOE_LORA_ERR_INVALID;
+    if (a->num_loras > 0 && (!a->a0 || !a->b0 || !a->lora_ranks || !a->scaling ||
+                             (a->out1 > 0 && (!a->a1 || !a->b1))))
+      return MOE_LORA_ERR_INVALID;
+  }
+  p->dtype = a->dtype;
+  p->T = a->num_tokens; p->H = a->hidden; p->N0 = a->out0; p->N1 = a->out1;
+  p->L = a->num_loras; p->R = a->num_loras > 0 ? a->max_rank : 0; p->BM = a->block_m;
+  p->x = a->x; p->w = a->w;
+  p->a0 = a->a0; p->a1 = a->a1; p->b0 = a->b0; p->b1 = a->b1;
+  p->lora_ranks = a->lora_ranks; p->scaling = a->scaling;
+  p->sorted_ids = a->sorted_pair_ids; p->tile_expert = a->tile_expert; p->tile_lora = a->tile_lora;
+  p->expert_tile_offsets = a->expert_tile_offsets; p->num_rows_padded = a->num_rows_padded;
+  p->y = a->y;
+  p->out_f32 = (a->out_dtype == MOE_LORA_F32) && a->dtype != MOE_LORA_F32;
+  return MOE_LORA_OK;
+}
+
+size_t moe_lora_dense_workspace_bytes(const moe_lora_dense_args* args) {
+  DenseProblem p;
+  if (to_dense(args, &p, false) != MOE_LORA_OK) return 0;
+  return dense_ws_layout(p).bytes;
+}
+
+static int dense_impl(const moe_lora_dense_args* args, void* stream, void* const* events) {
+  DenseProblem p;
+  int st = to_dense(args, &p, true);
+  if (st != MOE_LORA_OK) return st;
+  if (p.T == 0) return MOE_LORA_OK;
+  if (!args->workspace || args->workspace_bytes < dense_ws_layout(p).bytes) return MOE_LORA_ERR_WORKSPACE;
+  hipEvent_t ev[2 * kDenseNumStages];
+  if (events)
+    for (int i = 0; i < 2 * kDenseNumStages; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  return hip_status(launch_dense(p, args->workspace, static_cast<hipStream_t>(stream),
+                                 events ? ev : nullptr));
+}
+
+int moe_lora_dense_forward(const moe_lora_dense_args* args, void* stream) {
+  return dense_impl(args, stream, nullptr);
+}
+
+int moe_lora_dense_forward_events(const moe_lora_dense_args* args, void* stream,
+                                  void* const* events) {
+  if (!events) return MOE_LORA_ERR_INVALID;
+  return dense_impl(args, stream, events);
+}
+
 }  // extern "C"

@@ -457,6 +457,8 @@ struct GemmArgs {
   const float* topk_weights;
   int64_t cap;                // rows of sorted_ids / act / h
   int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
+  int64_t n_split;            // dense mode: output columns [0, n_split) use b_pool0 and h[:, :RP],
+                              // the rest b_pool1 and h[:, RP:2RP] (a multiple of 32)
 };
 
 
@@ -537,9 +539,17 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // W: weight element, T (bf16 / fp32 weights) or uint8_t (fp8 e4m3 codes with
-// 128 x 128 block scales; T = bf16)
-template <typename T, typename W, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int ROWB, bool GATE_UP>
+// 128 x 128 block scales; T = bf16).
+// GATE_UP: x rows gathered by pair, gate / up columns paired, SiLU(g) * u to act.
+// Otherwise the down form: A rows in sorted order, weighted rows scattered to z;
+// DENSE (with !GATE_UP): A rows gathered like gate_up, unit weights, and the
+// LoRA expand switches pools at column n_split (a projection whose output is
+// two slices with their own LoRA factors).
+template <typename T, typename W, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int ROWB, bool GATE_UP,
+          bool DENSE = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T> a) {
+  static_assert(!(GATE_UP && DENSE), "dense mode is a form of the down GEMM");
+  constexpr bool GATHER = GATE_UP || DENSE;       // A rows are x rows of the rows' pairs
   typedef Elt<T> E_;
   typedef Blk<T> B_;
   typedef typename E_::frag frag;
@@ -669,7 +679,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   auto grow_of = [&](int row, int pid_in) -> int64_t {
     if (row < BM) {
       const int r = row;
-      if (GATE_UP) {
+      if (GATHER) {
         const int pid = r < nrows ? pid_in : a.P;
         return pid < a.P ? pid / a.top_k : 0;
       }
@@ -684,7 +694,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   };
   uint32_t src_off[SEG_PER_WAVE];   // byte offsets from a_base / b_base
   int pidv[SEG_PER_WAVE];
-  if (GATE_UP) {
+  if (GATHER) {
     // pair ids of the gathered A rows: clamped, unconditional loads, issued together
 #pragma unroll
     for (int i = 0; i < SEG_PER_WAVE; ++i) {
@@ -922,6 +932,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // blocks', so the whole expand waits for memory about once.
   if (lora_here) {
     constexpr int MAXKS = 64 / KF;   // RP <= 64
+    // dense mode: column block j belongs to the second output slice
+    auto dense_second = [&](int j) -> bool {
+      return DENSE && a.n_split < a.n_out && col_of(j) >= a.n_split;
+    };
     // rank step ks of the pass serving slot l in block i: h of this lane's
     // row (the block's first row, zeroed later, if its group is not served)
     // and the B^T values of its column (rows q >= r never read: q clamped)
@@ -931,15 +945,21 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       const bool mine = lg[i][lrow / 16] == l;
       const float* hrow = a.h + (row0 + min(rb + (mine ? lrow : 0), nrows - 1)) * a.HS;
       hg = *reinterpret_cast<const floatx8*>(hrow + q0);
-      hu = GATE_UP ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
+      // the second h half exists for gate_up and for a dense output with two slices
+      hu = (GATE_UP || (DENSE && a.HS > a.RP)) ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const bool up = GATE_UP && j >= NB / 2;
+        // second pool: the up columns, or (dense, when the second slice is not
+        // empty) the columns past n_split; blocks past n_out (never stored)
+        // clamp into the last slice that exists
+        const bool up = GATE_UP ? j >= NB / 2 : dense_second(j);
         const T* pool = up ? a.b_pool1 : a.b_pool0;
-        const int64_t col = min(col_of(j) + lrow, a.n_out - 1);
-        const T* pb = pool + (((int64_t)max(l, 0) * a.E + e) * a.R) * a.n_out + col;
+        const int64_t c0 = DENSE && up ? a.n_split : 0;           // the pool's first column
+        const int64_t width = DENSE ? (up ? a.n_out - a.n_split : a.n_split) : a.n_out;
+        const int64_t col = min(col_of(j) + lrow, a.n_out - 1) - c0;
+        const T* pb = pool + (((int64_t)max(l, 0) * a.E + e) * a.R) * width + col;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) bfv[j][v] = pb[(int64_t)min(q0 + v, max(r, 1) - 1) * a.n_out];
+        for (int v = 0; v < 8; ++v) bfv[j][v] = pb[(int64_t)min(q0 + v, max(r, 1) - 1) * width];
       }
     };
     auto mma_step = [&](auto I, int l, int r, int ks, floatx8 hg, floatx8 hu, frag* bfv) {
@@ -955,7 +975,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const bool up = GATE_UP && j >= NB / 2;
+        const bool up = GATE_UP ? j >= NB / 2 : dense_second(j);
         const floatx8& hv = up ? hu : hg;
         if constexpr (sizeof(T) == 2) {
           // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
@@ -1050,7 +1070,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     for (int r = threadIdx.x; r < BM; r += 64 * NWAVES) {
       const int pid = a.sorted_ids[row0 + min(r, nrows - 1)];
       ep_pid[r] = r < nrows ? pid : a.P;
-      ep_w[r] = a.topk_weights[min(pid, a.P - 1)];
+      ep_w[r] = DENSE ? 1.0f : a.topk_weights[min(pid, a.P - 1)];
     }
     // the unweighted results, [WM rows][WN cols] fp32 per wave
     static_assert(NWAVES * WM * WN * 4 <= STAGES * STAGE_BYTES, "epilogue staging fits");
@@ -1447,6 +1467,156 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   }
   mark(2 * kStageCombine + 1);
   return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// dense projection with two LoRA output slices
+// --------------------------------------------------------------------------
+// K splits of the dense GEMM: a decode-sized batch has a handful of tiles
+// (one or two items times the column tiles), far fewer than the 256 CUs; each
+// K split is a tile of its own (one fp32 plane of z each, added in order by the
+// combine), up to 8, each at least 512 deep and a whole number of K tiles
+template <typename T>
+static int dense_ksplit(int64_t P, int64_t K, int64_t N) {
+  constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN_DOWN, BK = TileCfg<T>::ROWB / (int)sizeof(T);
+  const int64_t tiles = (ceil_div(P, BM) + 1) * ceil_div(N, BN);
+  const int64_t slots = 256 * (int64_t)TileCfg<T>::PER_CU;
+  if (P <= 0 || tiles >= slots / 2) return 1;
+  int s = (int)std::min<int64_t>(8, ceil_div(slots, tiles));
+  while (s > 1 && (K % (s * BK) != 0 || K / s < 512)) --s;
+  return s;
+}
+
+DenseWs dense_ws_layout(const DenseProblem& p) {
+  DenseWs w;
+  const int64_t P = p.T;   // one pair per token (E = 1, k = 1)
+  w.cap = align_capacity(P, 1, p.L, p.BM);
+  w.max_items = ceil_div(w.cap, rows_per_item(p.dtype)) + (P < 1 ? P : 1);
+  if (w.max_items < 1) w.max_items = 1;
+  w.RP = p.L > 0 ? round_up(p.R > 0 ? p.R : 1, 32) : 0;
+  w.npool = p.N1 > 0 ? 2 : 1;
+  w.split = shrink_splits(P, p.H, false);
+  w.ksplit = p.dtype == 1 ? dense_ksplit<bf16_t>(P, p.H, p.N0 + p.N1) : dense_ksplit<float>(P, p.H, p.N0 + p.N1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
+  w.items_off = take(sizeof(int4) * (size_t)w.max_items);
+  w.count_off = take(sizeof(int32_t) * 36);
+  w.h_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split * w.cap * w.npool * w.RP : 0);
+  w.z_off = take(sizeof(float) * (size_t)w.ksplit * P * (p.N0 + p.N1));
+  w.bytes = off;
+  return w;
+}
+
+template <typename T>
+static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t stream,
+                            hipEvent_t* events) {
+  auto mark = [&](int idx) {
+    if (events && events[idx]) (void)hipEventRecord(events[idx], stream);
+  };
+  const DenseWs w = dense_ws_layout(p);
+  char* ws = static_cast<char*>(workspace);
+  int4* items = reinterpret_cast<int4*>(ws + w.items_off);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + w.count_off);
+  float* h = reinterpret_cast<float*>(ws + w.h_off);
+  float* z = reinterpret_cast<float*>(ws + w.z_off);
+  const int64_t P = p.T, N = p.N0 + p.N1;
+  const bool lora = p.L > 0;
+  constexpr int BM = TileCfg<T>::BM, BND = TileCfg<T>::BN_DOWN, SD = TileCfg<T>::STAGES_DOWN;
+
+  mark(2 * kDenseStagePlan);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, 1, (int)p.BM, BM,
+                     p.expert_tile_offsets, items, count, (int)w.max_items);
+  mark(2 * kDenseStagePlan + 1);
+
+  const int64_t groups = w.cap / 16;
+  mark(2 * kDenseStageShrink);
+  if (lora && groups > 0 && P > 0) {
+    // h[:, :RP] = s x A0^T, h[:, RP:] = s x A1^T over the tokens' rows
+    ShrinkArgs<T> s{};
+    s.src = static_cast<const T*>(p.x);
+    s.sorted_ids = p.sorted_ids;
+    s.gathered = 1;
+    s.top_k = 1;
+    s.P = (int)P;
+    s.K = p.H;
+    s.pool0 = static_cast<const T*>(p.a0);
+    s.pool1 = static_cast<const T*>(p.a1);
+    s.R = (int)p.R; s.RP = (int)w.RP; s.L = (int)p.L; s.E = 1; s.BM = (int)p.BM;
+    s.tile_expert = p.tile_expert;
+    s.tile_lora = p.tile_lora;
+    s.num_rows_padded = p.num_rows_padded;
+    s.lora_ranks = p.lora_ranks;
+    s.scaling = p.scaling;
+    s.h = h;
+    s.cap = w.cap;
+    s.kchunk = shrink_kchunk(P, p.H, false);
+    s.split_stride = w.cap * w.npool * w.RP;
+    if (w.npool == 2)
+      launch_shrink<T, 2>(s, groups, w.split, false, stream);
+    else
+      launch_shrink<T, 1>(s, groups, w.split, false, stream);
+    if (w.split > 1)
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.npool * w.RP / 4, 256)),
+                         dim3(256), 0, stream, h, (int64_t)s.split_stride, w.split,
+                         p.num_rows_padded, (int)(w.npool * w.RP));
+  }
+  mark(2 * kDenseStageShrink + 1);
+
+  mark(2 * kDenseStageGemm);
+  if (P > 0) {
+    GemmArgs<T> a{};
+    a.items = items;
+    a.item_count = count;
+    a.max_items = (int)w.max_items;
+    a.top_k = 1;
+    a.P = (int)P;
+    a.sorted_ids = p.sorted_ids;
+    a.tile_lora = p.tile_lora;
+    a.expert_tile_offsets = p.expert_tile_offsets;
+    a.BM_tile = (int)p.BM;
+    a.lora_ranks = p.lora_ranks;
+    a.RP = (int)w.RP; a.R = (int)p.R; a.L = (int)p.L; a.E = 1;
+    a.topk_weights = nullptr;
+    a.cap = w.cap;
+    a.a_src = static_cast<const T*>(p.x);
+    a.K = p.H;
+    a.w = p.w;
+    a.n_out = N;
+    a.w_rows = N;
+    a.n_cols = (int)ceil_div(N, BND);
+    a.ksplit = w.ksplit;
+    a.n_tiles = a.n_cols * a.ksplit;
+    a.h = lora ? h : nullptr;
+    a.HS = w.npool * (int)w.RP;
+    a.b_pool0 = static_cast<const T*>(p.b0);
+    a.b_pool1 = static_cast<const T*>(p.b1);
+    a.n_split = p.N0;
+    a.z = z;
+    a.tile_ctr = count + 4;
+    const int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
+    hipLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false, true>),
+                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
+  }
+  mark(2 * kDenseStageGemm + 1);
+
+  mark(2 * kDenseStageCombine);
+  if (P > 0) {
+    const int64_t n4 = P * N / 4;
+    if (p.out_f32)
+      hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, z, static_cast<float*>(p.y), P, 1, N, w.ksplit, P * N);
+    else
+      hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, z, static_cast<T*>(p.y), P, 1, N, w.ksplit, P * N);
+  }
+  mark(2 * kDenseStageCombine + 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense(const DenseProblem& p, void* workspace, hipStream_t stream,
+                        hipEvent_t* events) {
+  if (p.dtype == 1) return run_dense<bf16_t>(p, workspace, stream, events);
+  return run_dense<float>(p, workspace, stream, events);
 }
 
 hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,

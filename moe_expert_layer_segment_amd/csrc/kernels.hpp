@@ -74,4 +74,27 @@ enum { kStagePlan = 0, kStageShrinkX, kStageGateUp, kStageShrinkA, kStageDown, k
 hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
                           hipEvent_t* events);
 
+// A dense projection with per-request LoRA whose output is two column slices
+// [0, N0) and [N0, N0 + N1), each with its own LoRA factors (N1 may be 0).
+struct DenseProblem {
+  int dtype;  // 0 = fp32, 1 = bf16
+  int64_t T, H, N0, N1, L, R, BM;
+  const void* x;                       // [T, H]
+  const void* w;                       // [N0 + N1, H]
+  const void *a0, *a1, *b0, *b1;       // [L, R, H] x2, [L, R, N0], [L, R, N1]
+  const int32_t* lora_ranks;
+  const float* scaling;
+  const int32_t *sorted_ids, *tile_expert, *tile_lora, *expert_tile_offsets, *num_rows_padded;
+  void* y;                             // [T, N0 + N1]
+  int out_f32;
+};
+struct DenseWs {
+  int64_t cap, max_items, RP;
+  int npool = 1, split = 1, ksplit = 1;   // shrink pools / shrink K splits / GEMM K splits
+  size_t items_off, count_off, h_off, z_off, bytes;
+};
+DenseWs dense_ws_layout(const DenseProblem& p);
+enum { kDenseStagePlan = 0, kDenseStageShrink, kDenseStageGemm, kDenseStageCombine, kDenseNumStages };
+hipError_t launch_dense(const DenseProblem& p, void* workspace, hipStream_t stream, hipEvent_t* events);
+
 }  // namespace moelora

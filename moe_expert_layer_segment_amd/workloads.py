@@ -333,3 +333,104 @@ def random_spec(rng: np.random.Generator, *, max_experts=6, max_k=3, max_dim=96,
     wi = [int(v) for v in rng.integers(-1, L, size=bs)] if L > 0 else [-1] * bs
     return LayerSpec(name, E, k, H, I, L, ranks, lens, wi, dtype=dtype,
                      seed=int(rng.integers(0, 2**31)), router="normal", pool_rank=R)
+
+
+# ----------------------------------------------------------------------------
+# second workload: a dense projection with per-request LoRA and a two-slice
+# output (the fused q_a_proj + kv_a_proj_with_mqa projection of MLA: outputs
+# of 1536 and 512 + 64 columns over a 7168-wide hidden state)
+# ----------------------------------------------------------------------------
+_TID_DW, _TID_DA0, _TID_DA1, _TID_DB0, _TID_DB1 = 20, 21, 22, 23, 24
+
+
+@dataclasses.dataclass
+class DenseSpec:
+    """One dense LoRA projection with outputs [0, out0) and [out0, out0 + out1)."""
+    name: str
+    hidden: int
+    out0: int
+    out1: int
+    num_loras: int
+    lora_ranks: List[int]
+    seg_lens: List[int]
+    weight_indices: List[int]
+    dtype: str = "bf16"
+    seed: int = 0
+    alpha_over_rank: float = 2.0
+    pool_rank: Optional[int] = None
+
+    @property
+    def num_tokens(self) -> int:
+        return int(sum(self.seg_lens))
+
+    @property
+    def num_reqs(self) -> int:
+        return len(self.seg_lens)
+
+    @property
+    def max_rank(self) -> int:
+        if self.pool_rank is not None:
+            return int(self.pool_rank)
+        return max([int(r) for r in self.lora_ranks] + [1])
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+def dense_config(name: str) -> DenseSpec:
+    if name == "d0":
+        return DenseSpec("d0_tiny_fp32", 256, 192, 64, 3, [8, 0, 16], [5, 1, 7, 3, 9],
+                         [2, 0, -1, 1, 2], dtype="f32", seed=40, pool_rank=16)
+    if name == "d1":
+        # the Mixtral-prefill batch's request structure (16 requests, 4096 tokens, 8 slots of
+        # rank 16 with slot 0 at rank 0, 2 requests without an adapter) on the MLA projection
+        c1 = config("c1")
+        return DenseSpec("d1_mla_qa_kva_prefill", 7168, 1536, 576, c1.num_loras, c1.lora_ranks,
+                         c1.seg_lens, c1.weight_indices, seed=41, pool_rank=16)
+    if name == "d2":
+        return DenseSpec("d2_mla_qa_kva_decode", 7168, 1536, 576, 32, [32] * 32, [1] * 64,
+                         [b % 32 for b in range(64)], seed=42, pool_rank=32)
+    raise KeyError(name)
+
+
+DENSE_CONFIG_NAMES = ("d0", "d1", "d2")
+
+
+def generate_dense(spec: DenseSpec, device="cpu", canary: bool = True,
+                   with_lora: bool = True) -> Dict[str, object]:
+    """Every input of the dense LoRA projection for ``spec`` (same conventions as
+    ``generate``: W ~ N(0, 1/H), A ~ N(0, 1/H), B ~ N(0, 0.01), rows past a
+    slot's rank NaN when ``canary``)."""
+    dev = torch.device(device)
+    dt = spec.torch_dtype
+    T, H, N0, N1 = spec.num_tokens, spec.hidden, spec.out0, spec.out1
+    L, R, s = spec.num_loras, spec.max_rank, spec.seed
+    seg_lens = np.asarray(spec.seg_lens, dtype=np.int64)
+    seg_indptr = np.zeros(len(seg_lens) + 1, dtype=np.int32)
+    seg_indptr[1:] = np.cumsum(seg_lens)
+    wi = np.asarray(spec.weight_indices, dtype=np.int32)
+    ranks = np.asarray(spec.lora_ranks, dtype=np.int32)
+    scaling = np.full(L, spec.alpha_over_rank, dtype=np.float32)
+    out: Dict[str, object] = {}
+    out["x"] = _randn((T, H), 1.0, _subseed(s, _TID_X), dev, dt)
+    out["w"] = _randn((N0 + N1, H), 1.0 / np.sqrt(H), _subseed(s, _TID_DW), dev, dt)
+    if with_lora and L > 0:
+        fill = float("nan") if canary else 0.0
+        for name, tid, dim, std in (("a0", _TID_DA0, H, 1.0 / np.sqrt(H)),
+                                    ("a1", _TID_DA1, H, 1.0 / np.sqrt(H)),
+                                    ("b0", _TID_DB0, N0, 0.1), ("b1", _TID_DB1, N1, 0.1)):
+            pool = torch.full((L, R, dim), fill, device=dev, dtype=dt)
+            for l in range(L):
+                r = int(ranks[l])
+                if r > 0 and dim > 0:
+                    pool[l, :r] = _randn((r, dim), std, _subseed(s, tid, l), dev, dt)
+            out[name] = pool
+    out["seg_indptr"] = torch.from_numpy(seg_indptr).to(dev)
+    out["weight_indices"] = torch.from_numpy(wi).to(dev)
+    out["lora_ranks"] = torch.from_numpy(ranks).to(dev)
+    out["scaling"] = torch.from_numpy(scaling).to(dev)
+    out["topk_ids"] = torch.zeros((T, 1), dtype=torch.int32, device=dev)
+    out["meta"] = dict(seg_indptr=seg_indptr, weight_indices=wi, lora_ranks=ranks,
+                       scaling=scaling, max_seg_len=int(seg_lens.max()) if len(seg_lens) else 0)
+    return out

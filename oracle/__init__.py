@@ -8,6 +8,7 @@ from .moe_lora_oracle import (  # noqa: F401
     UnderCoverError,
     align_capacity_rows,
     decode_e4m3,
+    dense_lora_forward,
     dequantize_block_fp8,
     moe_lora_align,
     moe_lora_forward,

@@ -361,3 +361,42 @@ def dequantize_block_fp8(codes, scales, block: int = 128) -> np.ndarray:
         raise ValueError("codes and scales do not tile into blocks")
     s_full = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)
     return w * s_full
+
+
+# ---------------------------------------------------------------------------
+# dense projection with a two-slice LoRA output (PR #22323 page, sections
+# 功能与动机 and 实现拆解 item 2: the fused q_a_proj + kv_a_proj_with_mqa
+# projection of MLA, outputs of unequal size, LoRA B split in two and applied
+# per output part).  Reading: each output slice i has its own LoRA factors
+# (A_i, B_i); the slot of a token and its masking are those of the MoE layer.
+# ---------------------------------------------------------------------------
+def dense_lora_forward(x, w, n0: int, lora_ranks, scaling, token_lora_mapping,
+                       adapter_enabled, a0=None, a1=None, b0=None, b1=None,
+                       tokens=None) -> np.ndarray:
+    """y [T, N0 + N1] float64:
+    y[t, :N0] = x_t W[:N0]^T + on_t s_l (x_t A0[l, :r]^T) B0[l, :r]
+    y[t, N0:] = x_t W[N0:]^T + on_t s_l (x_t A1[l, :r]^T) B1[l, :r]
+    with B stored transposed (rank-major, [L, R, out]) and on_t as in
+    moe_lora_forward.  ``tokens``: compute only these rows (same order)."""
+    X = _f64(x)
+    W = _f64(w)
+    T = X.shape[0]
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    X = X[rows]
+    y = X @ W.T
+    N0 = int(n0)
+    mapping = np.asarray(token_lora_mapping, dtype=np.int64)[rows]
+    ranks = np.asarray(lora_ranks, dtype=np.int64)
+    scal = np.asarray(scaling, dtype=np.float64)
+    if a0 is None or len(ranks) == 0:
+        return y
+    for l in np.unique(mapping):
+        l = int(l)
+        if not _lora_on(l, adapter_enabled, ranks):
+            continue
+        m = mapping == l
+        r, s = int(ranks[l]), scal[l]
+        y[m, :N0] += s * ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])
+        if y.shape[1] > N0:
+            y[m, N0:] += s * ((X[m] @ _f64(a1[l])[:r].T) @ _f64(b1[l])[:r])
+    return y

@@ -513,4 +513,67 @@ def pin_block_dequant(orc):
     assert np.array_equal(d, mask)
 
 
+# ---------------------------------------------------------------------------
+# dense two-slice LoRA projection
+# ---------------------------------------------------------------------------
+def _dense_case(seed=0, **kw):
+    spec = workloads.DenseSpec("dpin", kw.get("H", 64), kw.get("N0", 48), kw.get("N1", 32), 3,
+                               kw.get("ranks", [4, 0, 8]), [3, 2, 4, 1], [0, 1, 2, -1],
+                               dtype="f32", seed=seed, pool_rank=8)
+    inp = workloads.generate_dense(spec, device="cpu", canary=kw.get("canary", True))
+    m = inp["meta"]
+    en = np.array([1 if (l in set(m["weight_indices"].tolist()) and m["lora_ranks"][l] > 0) else 0
+                   for l in range(spec.num_loras)], dtype=np.int32)
+    mp = np.repeat(m["weight_indices"], np.diff(m["seg_indptr"])).astype(np.int32)
+    f = {k: inp[k].double().numpy() for k in ("x", "w", "a0", "a1", "b0", "b1")}
+    return spec, inp, m, en, mp, f
+
+
+def _dense_call(orc, spec, m, en, mp, f, **over):
+    kw = dict(a0=f["a0"], a1=f["a1"], b0=f["b0"], b1=f["b1"])
+    kw.update(over)
+    return orc.dense_lora_forward(f["x"], f["w"], spec.out0, m["lora_ranks"], m["scaling"], mp, en,
+                                  **kw)
+
+
+def pin_dense_vs_torch_linear(orc):
+    spec, inp, m, en, mp, f = _dense_case(seed=3)
+    y = _dense_call(orc, spec, m, en, mp, f)
+    x = torch.from_numpy(f["x"])
+    N0 = spec.out0
+    for t in range(spec.num_tokens):
+        l = int(mp[t])
+        w0 = torch.from_numpy(f["w"][:N0].copy())
+        w1 = torch.from_numpy(f["w"][N0:].copy())
+        if l >= 0 and en[l] and m["lora_ranks"][l] > 0:
+            r, sc = int(m["lora_ranks"][l]), float(m["scaling"][l])
+            w0 = w0 + sc * torch.from_numpy(f["b0"][l, :r].T.copy()) @ torch.from_numpy(f["a0"][l, :r].copy())
+            w1 = w1 + sc * torch.from_numpy(f["b1"][l, :r].T.copy()) @ torch.from_numpy(f["a1"][l, :r].copy())
+        ref = torch.cat([F.linear(x[t], w0), F.linear(x[t], w1)]).numpy()
+        assert np.allclose(y[t], ref, rtol=1e-10, atol=1e-12), t
+
+
+def pin_dense_reductions(orc):
+    spec, inp, m, en, mp, f = _dense_case(seed=4, canary=False)
+    base = f["x"] @ f["w"].T
+    # no pools, and zero B, give the plain projection
+    assert np.allclose(orc.dense_lora_forward(f["x"], f["w"], spec.out0, m["lora_ranks"],
+                                              m["scaling"], mp, en), base, rtol=1e-12, atol=1e-12)
+    z = _dense_call(orc, spec, m, en, mp, f, b0=np.zeros_like(f["b0"]), b1=np.zeros_like(f["b1"]))
+    assert np.allclose(z, base, rtol=1e-12, atol=1e-12)
+    # each slice's factors move only that slice
+    y = _dense_call(orc, spec, m, en, mp, f)
+    y2 = _dense_call(orc, spec, m, en, mp, f, a1=f["a1"] * 2.0)
+    N0 = spec.out0
+    assert np.array_equal(y[:, :N0], y2[:, :N0]) and not np.allclose(y[:, N0:], y2[:, N0:])
+    y3 = _dense_call(orc, spec, m, en, mp, f, b0=f["b0"] * -1.0)
+    assert np.array_equal(y[:, N0:], y3[:, N0:]) and not np.allclose(y[:, :N0], y3[:, :N0])
+    # tokens without a live slot get the plain projection
+    off = np.array([(l < 0) or (not en[l]) or m["lora_ranks"][l] == 0 for l in mp])
+    assert off.any() and np.allclose(y[off], base[off], rtol=1e-12, atol=1e-12)
+    # a token subset is the same rows
+    sub = np.array([5, 0, 7])
+    assert np.allclose(_dense_call(orc, spec, m, en, mp, f, tokens=sub), y[sub], rtol=1e-12, atol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

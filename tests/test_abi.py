@@ -188,6 +188,46 @@ def test_forward_fp8_weight_validation():
     assert ws8 == lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
 
 
+def _dargs(**over):
+    a = binding.DenseArgs()
+    a.struct_size = ctypes.sizeof(binding.DenseArgs)
+    a.dtype = binding.DTYPE_BF16
+    a.num_tokens, a.hidden, a.out0, a.out1 = 8, 128, 192, 64
+    a.num_loras, a.max_rank, a.block_m = 2, 16, 16
+    for n, _ in binding.DenseArgs._fields_:
+        if n not in ("struct_size", "dtype", "num_tokens", "hidden", "out0", "out1", "num_loras",
+                     "max_rank", "block_m", "workspace_bytes", "out_dtype"):
+            setattr(a, n, 0x1000)
+    a.workspace_bytes = 1
+    a.out_dtype = binding.DTYPE_BF16
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_dense_validation_codes():
+    lib = binding.lib()
+    call = lambda **o: lib.moe_lora_dense_forward(ctypes.byref(_dargs(**o)), None)  # noqa: E731
+    assert call() == binding.ERR_WORKSPACE                     # valid but a 1-byte workspace
+    assert call(dtype=7) == binding.ERR_UNSUPPORTED
+    assert call(out_dtype=binding.DTYPE_F32) == binding.ERR_WORKSPACE
+    assert call(struct_size=8) == binding.ERR_INVALID
+    assert call(out0=0) == binding.ERR_INVALID
+    assert call(out1=-64) == binding.ERR_INVALID
+    assert call(out0=100) == binding.ERR_UNSUPPORTED
+    assert call(out1=96) == binding.ERR_UNSUPPORTED
+    assert call(hidden=100) == binding.ERR_UNSUPPORTED
+    assert call(max_rank=65) == binding.ERR_UNSUPPORTED
+    assert call(block_m=24) == binding.ERR_INVALID
+    assert call(w=None) == binding.ERR_INVALID
+    assert call(b1=None) == binding.ERR_INVALID
+    assert call(out1=0, a1=None, b1=None) == binding.ERR_WORKSPACE   # one slice needs no second pool
+    assert call(num_loras=0, a0=None, b0=None, a1=None, b1=None) == binding.ERR_WORKSPACE
+    assert call(num_tokens=0) == binding.OK
+    ws = lib.moe_lora_dense_workspace_bytes(ctypes.byref(_dargs()))
+    assert ws > 0 and lib.moe_lora_dense_workspace_bytes(ctypes.byref(_dargs(dtype=9))) == 0
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):

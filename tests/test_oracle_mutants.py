@@ -40,6 +40,12 @@ MUTANTS = {
     "e4m3_subnormal_scale": ("subnormal = man * 2.0 ** -9", "subnormal = man * 2.0 ** -10"),
     "e4m3_no_nan": ("return np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, v)", "return v"),
     "dequant_scale_dropped": ("    return w * s_full", "    return w"),
+    "dense_a0_for_both": ("y[m, N0:] += s * ((X[m] @ _f64(a1[l])[:r].T) @ _f64(b1[l])[:r])",
+                          "y[m, N0:] += s * ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b1[l])[:r])"),
+    "dense_no_scaling": ("y[m, :N0] += s * ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])",
+                         "y[m, :N0] += ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])"),
+    "dense_full_pool_rows": ("y[m, :N0] += s * ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])",
+                             "y[m, :N0] += s * ((X[m] @ _f64(a0[l]).T) @ _f64(b0[l]))"),
     "brute_b_untransposed": ("Bd = _f64(b_down[l, e])[:r].T      # [H, r]", "Bd = _f64(b_down[l, e])[:r].T[::-1]"),
 }
 
