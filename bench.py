@@ -62,7 +62,7 @@ def _stage_of(kname):
         return "shrink_reduce"
     if "shrink_kernel" in kname:
         return "shrink_gate_up" if ("Li2E" in kname or ", 2>" in kname) else "shrink_down"
-    for key in ("combine", "plan", "info", "align_count", "align_scan", "align_scatter"):
+    for key in ("combine", "plan", "tile_table", "info", "align_count", "align_scan", "align_scatter"):
         if key + "_kernel" in kname:
             return key
     return None

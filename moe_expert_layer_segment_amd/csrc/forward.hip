@@ -71,6 +71,70 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
 }
 
 // --------------------------------------------------------------------------
+// tile tables: the persistent GEMMs' logical tile order, one record per tile,
+// so a workgroup finds its tile with one load instead of a chain of dependent
+// ones; and each align block's LoRA slot with its rank in one word
+// --------------------------------------------------------------------------
+// Logical tiles are ordered expert by expert.  An expert's n_e work items are
+// cut into round(n_e / 8) near-equal groups, and a group's tiles are
+// column-major with its items fastest, so a weight column tile is fetched
+// once per group and shared by its items.  (About 8 items per group balances
+// the x rows and the weight columns that a window of 32 resident tiles
+// fetches: a 128-row x tile is half a 256-row weight tile.)  Record:
+// {first row, rows, expert, column tile x K split}; rows = 0 marks a tile
+// past the item count.
+__device__ inline int4 gemm_tile_of(const int4* items, int count, int n_tiles, const int32_t* eto,
+                                    int BM_tile, int E, int rows_per_item, int logical) {
+  const int4 skip = make_int4(0, 0, 0, -1);
+  // the expert group of logical tile `logical` spans its items' range times
+  // n_tiles, so item logical / n_tiles belongs to it
+  const int4 in_group = items[logical / n_tiles];
+  const int first = in_group.w, eg = in_group.z;
+  if (eg < 0 || eg >= E || first < 0 || first > logical / n_tiles) return skip;
+  const int rows_e = (eto[eg + 1] - eto[eg]) * BM_tile;
+  const int n_e = (rows_e + rows_per_item - 1) / rows_per_item;   // the expert's items
+  if (n_e <= 0) return skip;
+  const int ng = max(1, (n_e + 4) / 8);
+  const int gbase = n_e / ng, grem = n_e % ng;   // groups 0..grem-1 have gbase+1 items
+  const int li = logical / n_tiles - first;      // an item index inside the group
+  const int gj = li < grem * (gbase + 1) ? li / (gbase + 1) : grem + (li - grem * (gbase + 1)) / gbase;
+  const int g_off = gj * gbase + min(gj, grem);  // the group's first item
+  const int g_n = gbase + (gj < grem ? 1 : 0);
+  const int local = logical - (first + g_off) * n_tiles;
+  const int item_idx = first + g_off + local % g_n;
+  const int col_t = local / g_n;                 // column tile x K split
+  if (item_idx >= count || col_t >= n_tiles) return skip;
+  const int4 item = items[item_idx];
+  if (item.z != eg) return skip;
+  return make_int4(item.x, item.y, item.z, col_t);
+}
+
+// slot_rank[b] = slot | rank << 16 of align block b (rank = min(r_l, R)), or
+// -1 when the block has no LoRA (slot -1, outside [0, L), or rank 0)
+__global__ void __launch_bounds__(256)
+tile_table_kernel(const int4* __restrict__ items, const int32_t* __restrict__ item_count, int max_items,
+                  const int32_t* __restrict__ expert_tile_offsets, int BM_tile, int E, int rows_per_item,
+                  int n_tiles0, int4* __restrict__ tab0, int n_tiles1, int4* __restrict__ tab1,
+                  const int32_t* __restrict__ tile_lora, const int32_t* __restrict__ lora_ranks, int L,
+                  int R, int n_blocks, int32_t* __restrict__ slot_rank) {
+  const int count = min(item_count[0], max_items);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t n0 = (int64_t)count * n_tiles0, n1 = tab1 ? (int64_t)count * n_tiles1 : 0;
+  const int64_t n = max(max(n0, n1), (int64_t)(slot_rank ? n_blocks : 0));
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    if (i < n0)
+      tab0[i] = gemm_tile_of(items, count, n_tiles0, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i);
+    if (i < n1)
+      tab1[i] = gemm_tile_of(items, count, n_tiles1, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i);
+    if (slot_rank && i < n_blocks) {
+      const int l = tile_lora[i];
+      const int r = (l >= 0 && l < L) ? min(lora_ranks[l], R) : 0;
+      slot_rank[i] = r > 0 ? (l | (r << 16)) : -1;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // shrink: h[row, pool*RP + q] = s_l * sum_k a_src[row, k] * A_pool[l, e, q, k]
 // for q < r_l (zero for r_l <= q < RP).  One workgroup per (16-row group, K
 // split); with more than one split, split c writes its partial sums to its
@@ -457,6 +521,8 @@ struct GemmArgs {
   const float* topk_weights;
   int64_t cap;                // rows of sorted_ids / act / h
   int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
+  const int4* tile_tab;       // [item count x n_tiles] logical tile records (tile_table_kernel)
+  const int32_t* slot_rank;   // [cap / BM_tile] slot | rank << 16 per align block, or -1
   int64_t n_split;            // dense mode: output columns [0, n_split) use b_pool0 and h[:, :RP],
                               // the rest b_pool1 and h[:, RP:2RP] (a multiple of 32)
 };
@@ -584,14 +650,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   constexpr int MAXKB = 128;      // K / 128 per tile (K <= 16384)
   __shared__ float sc_lds[WF8 ? NWAVES * NB * MAXKB : 1];
 
-  // Persistent tile loop.  Logical tiles are ordered expert by expert, and
-  // inside an expert by groups of its work items, column-major with the
-  // group's items fastest, so a weight column tile is fetched once per group
-  // and shared by its items.  Workgroups are dealt round-robin over the 8 XCDs; each XCD owns a
-  // contiguous range of logical tiles, handed out in order by a per-XCD
-  // counter, so the tiles resident on one XCD at any time are a sliding
-  // window of neighbours sharing x rows and weight columns in its L2.  A
-  // workgroup claims its next tile when it starts the current one.
+  // Persistent tile loop over the logical tile order of tile_table_kernel
+  // (expert by expert; inside an expert, groups of about 8 work items whose
+  // tiles are column-major, items fastest).  Workgroups are dealt round-robin
+  // over the 8 XCDs; each XCD owns a contiguous range of logical tiles, handed
+  // out in order by a per-XCD counter, so the tiles resident on one XCD at any
+  // time are a sliding window of neighbours sharing x rows and weight columns
+  // in its L2.  A workgroup claims its next tile when it starts the current
+  // one and loads the next tile's record before the current epilogue.
   const int count = min(a.item_count[0], a.max_items);
   const int total = count * a.n_tiles;
   const int xcd = blockIdx.x % 8;
@@ -600,45 +666,27 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   __shared__ int claimed;
   if (threadIdx.x == 0) claimed = atomicAdd(&a.tile_ctr[xcd], 1);
   __syncthreads();
-  int logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);   // uniform: scalar loads of the tile's metadata
+  int logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);
+  // the record of tile `logical` (a clamped, always valid index when the loop runs)
+  int4 desc = a.tile_tab[max(min(logical, t_end - 1), 0)];
   while (logical < t_end) {
   int next_claim = 0;
   if (threadIdx.x == 0) next_claim = atomicAdd(&a.tile_ctr[xcd], 1);
   bool published = false;   // the next claim was written to LDS inside the tile
+  bool have_next = false;   // next_desc holds the next tile's record
+  int4 next_desc;
   [&]() {
-  // the expert group of logical tile `logical` spans its items' range times
-  // n_tiles, so item logical / n_tiles belongs to it
-  const int4 in_group = a.items[logical / a.n_tiles];
-  const int first = in_group.w, eg = in_group.z;
-  if (eg < 0 || eg >= a.E || first < 0 || first > logical / a.n_tiles) return;
-  const int rows_e = (a.expert_tile_offsets[eg + 1] - a.expert_tile_offsets[eg]) * a.BM_tile;
-  const int n_e = (rows_e + BM - 1) / BM;   // the expert's items
-  if (n_e <= 0) return;
-  // The expert's items are cut into round(n_e / 8) near-equal groups; a
-  // group's tiles are column-major, its items fastest.  (About 8 items per
-  // group balances the x rows and the weight columns a window of 32 resident
-  // tiles fetches: a 128-row x tile is half a 256-row weight tile.)
-  const int ng = max(1, (n_e + 4) / 8);
-  const int gbase = n_e / ng, grem = n_e % ng;   // groups 0..grem-1 have gbase+1 items
-  const int li = logical / a.n_tiles - first;    // an item index inside the group
-  const int gj = li < grem * (gbase + 1) ? li / (gbase + 1) : grem + (li - grem * (gbase + 1)) / gbase;
-  const int g_off = gj * gbase + min(gj, grem);  // the group's first item
-  const int g_n = gbase + (gj < grem ? 1 : 0);
-  const int local = logical - (first + g_off) * a.n_tiles;
-  const int item_idx = first + g_off + local % g_n;
-  const int col_t = local / g_n;                 // column tile x K split
-  if (item_idx >= count || col_t >= a.n_tiles) return;
+  const int col_t = desc.w;
+  const int64_t row0 = desc.x;
+  const int nrows = desc.y;
+  const int e = desc.z;
+  if (col_t < 0 || col_t >= a.n_tiles || row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) ||
+      (row0 & 15) || row0 + nrows > a.cap || e < 0 || e >= a.E)
+    return;
   const int split = col_t / a.n_cols;            // K split (split-major: a window shares its x rows)
   const int ntile = col_t - split * a.n_cols;
   const int64_t kper = a.K / a.ksplit;           // K elements per split, a multiple of BK
   const bool lora_here = a.h != nullptr && split == 0;   // the expand is added once
-  const int4 item = a.items[item_idx];
-  const int64_t row0 = item.x;
-  const int nrows = item.y;
-  const int e = item.z;
-  if (row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) || (row0 & 15) || row0 + nrows > a.cap ||
-      e < 0 || e >= a.E)
-    return;
   __syncthreads();  // the previous tile's last LDS reads are done
 
   // wave index in an SGPR: every wave-level test below is a scalar branch
@@ -702,6 +750,34 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       pidv[i] = a.sorted_ids[row0 + min(min(row, BM - 1), nrows - 1)];
     }
   }
+  // LoRA slot table of this wave's row blocks, loaded with the pair ids and
+  // resolved before the first DMA, so the expand (ahead of the K loop) waits
+  // for its operands together with the ring's first stages: lg[i][g] = slot
+  // of 16-row group g of block i (-1: none or rank 0), rg[i][g] its rank;
+  // p0[i] = slot of the block's first pass (its first served group), r0[i]
+  // its rank.
+  constexpr int NG = BS / 16;
+  int lg[MB][NG], rg[MB][NG], p0[MB], r0[MB];
+  if (lora_here) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int rb = wm * WM + i * BS;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int r16 = max(min(rb + 16 * g, nrows - 16), 0);   // clamped: loads stay unconditional
+        const int sr = a.slot_rank[(row0 + r16) / a.BM_tile];
+        const bool on = rb + 16 * g < nrows && sr >= 0;
+        lg[i][g] = on ? (sr & 0xFFFF) : -1;
+        rg[i][g] = on ? (sr >> 16) : 0;
+      }
+      int l = -1, r = 0;
+#pragma unroll
+      for (int g = NG - 1; g >= 0; --g)
+        if (lg[i][g] >= 0) { l = lg[i][g]; r = rg[i][g]; }
+      p0[i] = l;
+      r0[i] = r;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < SEG_PER_WAVE; ++i) {
     const int seg = wave * SEG_PER_WAVE + i;
@@ -722,6 +798,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // issued after it were just waited for.)
   if (threadIdx.x == 0) claimed = next_claim;
   published = true;
+  if (lora_here) {
+    // the slot table is needed by the expand's loads: wait for it here, not
+    // after the DMA below (the counter would then take the DMA along)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) asm volatile("" ::"v"(p0[i]), "v"(r0[i]));
+  }
 
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   // this wave's DMA instructions [I0, I1) of one stage
@@ -791,32 +873,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < B_::ACC; ++v) acc[i][j][v] = 0.0f;
-
-  // LoRA slot table of this wave's row blocks, read before the K loop so the
-  // expand after it does not wait on these dependent loads: lg[i][g] = slot
-  // of 16-row group g of block i (-1: none or rank 0); p0[i] = slot of the
-  // block's first pass (its first served group), r0[i] its rank.
-  constexpr int NG = BS / 16;
-  int lg[MB][NG], p0[MB], r0[MB];
-  if (lora_here) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int rb = wm * WM + i * BS;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int r16 = max(min(rb + 16 * g, nrows - 16), 0);   // clamped: loads stay unconditional
-        const int l = a.tile_lora[(row0 + r16) / a.BM_tile];
-        const int lr = (l >= 0 && l < a.L) ? a.lora_ranks[l] : 0;
-        lg[i][g] = (rb + 16 * g < nrows && l >= 0 && l < a.L && lr > 0) ? l : -1;
-      }
-      int l = -1;
-#pragma unroll
-      for (int g = NG - 1; g >= 0; --g)
-        if (lg[i][g] >= 0) l = lg[i][g];
-      p0[i] = l;
-      r0[i] = l >= 0 ? min(a.lora_ranks[l], a.R) : 0;
-    }
-  }
 
   // Fragments are double-buffered in registers: the LDS reads of sub-step
   // ks+1 are issued before the MFMAs of sub-step ks.
@@ -902,10 +958,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       });
       __builtin_amdgcn_sched_barrier(0);
     };
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-      if (st < nk) issue_stage(st, st);
-    if constexpr (WF8) fill_scales();
     int s = 0;
     // steady state: STAGES-1 tiles are in flight at each wait
     for (; s + STAGES - 1 < nk; ++s) {
@@ -918,13 +970,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       compute(s % STAGES, -1, 0, s);
     }
   };
-  if (wm * WM + WM <= nrows)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
-  __builtin_amdgcn_s_barrier();   // everyone is done reading the ring
+  // the ring's first STAGES-1 stages
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue_stage(st, st);
+  if constexpr (WF8) fill_scales();
 
-  // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols] ------------------
+  // ---- LoRA expand: acc = h[rows, q] * Bpool[l, e, q, cols], before the K loop --
+  // Its operand loads go out right after the ring's first stages, so both
+  // latencies overlap, and its MFMAs start the accumulators.
   // Each 16-row group has its own slot; a BS-row block holds BS/16 groups, so
   // every distinct slot of the block gets its own pass with the rows of the
   // other slots masked to zero.  The first pass of every block (usually the
@@ -993,9 +1047,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       }
     };
     // one pass: rank steps from ks0 on (ks0 = 1: step 0 already done)
-    auto pass_rest = [&](auto I, int l, int ks0) {
+    auto pass_rest = [&](auto I, int l, int rk, int ks0) {
       constexpr int i = decltype(I)::value;
-      const int r = min(a.lora_ranks[l], a.R);
+      const int r = rk;
       const int nks = (r + KF - 1) / KF;
 #pragma unroll
       for (int ks = 1; ks < MAXKS; ++ks) {
@@ -1014,7 +1068,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       constexpr int i = decltype(I)::value;
       if (p0[i] < 0) return;
       mma_step(I, p0[i], r0[i], 0, hg0[i], hu0[i], bf0[i]);
-      pass_rest(I, p0[i], 1);
+      pass_rest(I, p0[i], r0[i], 1);
     });
     // further passes: groups whose slot differs from every earlier group's
     static_for<MB>([&](auto I) {
@@ -1026,15 +1080,28 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 #pragma unroll
         for (int g2 = 0; g2 < g; ++g2) seen = seen || lg[i][g2] == l;
         if (seen) continue;
-        const int r = min(a.lora_ranks[l], a.R);
+        const int r = rg[i][g];
         floatx8 hg, hu;
         frag bfv[NB];
         load_step(i, l, r, 0, hg, hu, bfv);
         mma_step(I, l, r, 0, hg, hu, bfv);
-        pass_rest(I, l, 1);
+        pass_rest(I, l, r, 1);
       }
     });
   }
+
+  if (wm * WM + WM <= nrows)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
+  __builtin_amdgcn_s_barrier();   // everyone is done reading the ring
+
+  // the next tile's record, loaded now so that it has arrived when the
+  // epilogue's stores are done (the claim was published before the K loop,
+  // whose barriers made it visible)
+  next_desc = a.tile_tab[max(min(t_begin + __builtin_amdgcn_readfirstlane(claimed), t_end - 1), 0)];
+  have_next = true;
+
 
   // ---- epilogue -------------------------------------------------------------
   // Results go through this wave's own LDS region (the ring is idle after the
@@ -1106,6 +1173,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     __syncthreads();
   }
   logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);
+  if (!have_next) next_desc = a.tile_tab[max(min(logical, t_end - 1), 0)];
+  desc = next_desc;
   }  // persistent tile loop
 }
 
@@ -1272,11 +1341,21 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.shrink4 = use_shrink4(P, p.E, p.L);
   w.split_gu = shrink_splits(P, p.H, w.shrink4);
   w.split_d = shrink_splits(P, p.I, w.shrink4);
+  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
+                                : down_ksplit<float>(P, p.E, p.H, p.I, false);
+  if (p.dtype == 1) {
+    w.n_tiles_gu = ceil_div(p.I, TileCfg<bf16_t>::BN / 2);
+    w.n_tiles_dn = ceil_div(p.H, TileCfg<bf16_t>::BN_DOWN) * w.split_down_k;
+  } else {
+    w.n_tiles_gu = ceil_div(p.I, TileCfg<float>::BN / 2);
+    w.n_tiles_dn = ceil_div(p.H, TileCfg<float>::BN_DOWN) * w.split_down_k;
+  }
+  w.tab_gu_off = take(sizeof(int4) * (size_t)w.max_items * w.n_tiles_gu);
+  w.tab_dn_off = take(sizeof(int4) * (size_t)w.max_items * w.n_tiles_dn);
+  w.slot_rank_off = take(sizeof(int32_t) * (size_t)(w.cap / p.BM + 1));
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
-  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
-                                : down_ksplit<float>(P, p.E, p.H, p.I, false);
   w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
   w.bytes = off;
   return w;
@@ -1307,6 +1386,17 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   mark(2 * kStagePlan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, (int)p.E, (int)p.BM, BM,
                      p.expert_tile_offsets, items, count, (int)w.max_items);
+  int4* tab_gu = reinterpret_cast<int4*>(ws + w.tab_gu_off);
+  int4* tab_dn = reinterpret_cast<int4*>(ws + w.tab_dn_off);
+  int32_t* slot_rank = reinterpret_cast<int32_t*>(ws + w.slot_rank_off);
+  {
+    const int64_t n = std::max<int64_t>(w.max_items * std::max(w.n_tiles_gu, w.n_tiles_dn), w.cap / p.BM);
+    hipLaunchKernelGGL(tile_table_kernel, dim3((unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(n, 256)))),
+                       dim3(256), 0, stream, items, count, (int)w.max_items, p.expert_tile_offsets,
+                       (int)p.BM, (int)p.E, BM, (int)w.n_tiles_gu, tab_gu, (int)w.n_tiles_dn, tab_dn,
+                       p.tile_lora, p.lora_ranks, (int)p.L, (int)p.R, (int)(w.cap / p.BM),
+                       lora ? slot_rank : nullptr);
+  }
   mark(2 * kStagePlan + 1);
 
   const int64_t groups = w.cap / 16;
@@ -1353,6 +1443,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   g.RP = (int)w.RP; g.R = (int)p.R; g.L = (int)p.L; g.E = (int)p.E;
   g.topk_weights = p.topk_weights;
   g.cap = w.cap;
+  g.slot_rank = slot_rank;
 
   // gate_up
   {
@@ -1366,6 +1457,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.n_cols = (int)ceil_div(p.I, BN / 2);
     a.ksplit = 1;
     a.n_tiles = a.n_cols;
+    a.tile_tab = tab_gu;
     a.h = lora ? hgu : nullptr;
     a.HS = 2 * (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b_gate);
@@ -1431,6 +1523,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.n_cols = (int)ceil_div(p.H, BND);
     a.ksplit = w.split_down_k;
     a.n_tiles = a.n_cols * a.ksplit;
+    a.tile_tab = tab_dn;
     a.h = lora ? hd : nullptr;
     a.HS = (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b_down);
@@ -1499,8 +1592,11 @@ DenseWs dense_ws_layout(const DenseProblem& p) {
   w.ksplit = p.dtype == 1 ? dense_ksplit<bf16_t>(P, p.H, p.N0 + p.N1) : dense_ksplit<float>(P, p.H, p.N0 + p.N1);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
+  w.n_tiles = ceil_div(p.N0 + p.N1, p.dtype == 1 ? TileCfg<bf16_t>::BN_DOWN : TileCfg<float>::BN_DOWN) * w.ksplit;
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
   w.count_off = take(sizeof(int32_t) * 36);
+  w.tab_off = take(sizeof(int4) * (size_t)w.max_items * w.n_tiles);
+  w.slot_rank_off = take(sizeof(int32_t) * (size_t)(w.cap / p.BM + 1));
   w.h_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split * w.cap * w.npool * w.RP : 0);
   w.z_off = take(sizeof(float) * (size_t)w.ksplit * P * (p.N0 + p.N1));
   w.bytes = off;
@@ -1526,6 +1622,15 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
   mark(2 * kDenseStagePlan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, 1, (int)p.BM, BM,
                      p.expert_tile_offsets, items, count, (int)w.max_items);
+  int4* tab = reinterpret_cast<int4*>(ws + w.tab_off);
+  int32_t* slot_rank = reinterpret_cast<int32_t*>(ws + w.slot_rank_off);
+  {
+    const int64_t n = std::max<int64_t>(w.max_items * w.n_tiles, w.cap / p.BM);
+    hipLaunchKernelGGL(tile_table_kernel, dim3((unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(n, 256)))),
+                       dim3(256), 0, stream, items, count, (int)w.max_items, p.expert_tile_offsets,
+                       (int)p.BM, 1, BM, (int)w.n_tiles, tab, 0, (int4*)nullptr, p.tile_lora,
+                       p.lora_ranks, (int)p.L, (int)p.R, (int)(w.cap / p.BM), lora ? slot_rank : nullptr);
+  }
   mark(2 * kDenseStagePlan + 1);
 
   const int64_t groups = w.cap / 16;
@@ -1586,6 +1691,9 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     a.n_cols = (int)ceil_div(N, BND);
     a.ksplit = w.ksplit;
     a.n_tiles = a.n_cols * a.ksplit;
+    if (a.n_tiles != w.n_tiles) return hipErrorInvalidValue;   // the table's tile count
+    a.tile_tab = tab;
+    a.slot_rank = slot_rank;
     a.h = lora ? h : nullptr;
     a.HS = w.npool * (int)w.RP;
     a.b_pool0 = static_cast<const T*>(p.b0);

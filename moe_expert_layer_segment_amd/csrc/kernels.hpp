@@ -62,7 +62,9 @@ struct ForwardProblem {
 
 struct ForwardWs {
   int64_t cap, max_items, RP;
-  size_t items_off, count_off, hgu_off, act_off, hd_off, z_off, bytes;
+  int64_t n_tiles_gu = 0, n_tiles_dn = 0;   // column tiles (x K splits) of the two GEMMs
+  size_t items_off, count_off, tab_gu_off, tab_dn_off, slot_rank_off, hgu_off, act_off, hd_off, z_off,
+      bytes;
   int split_gu = 1, split_d = 1;   // K splits of the two shrinks
   bool shrink4 = false;            // shrinks share pool rows across 4 row groups
   int split_down_k = 1;            // K splits of the down GEMM (planes of z)
@@ -91,7 +93,8 @@ struct DenseProblem {
 struct DenseWs {
   int64_t cap, max_items, RP;
   int npool = 1, split = 1, ksplit = 1;   // shrink pools / shrink K splits / GEMM K splits
-  size_t items_off, count_off, h_off, z_off, bytes;
+  int64_t n_tiles = 0;                    // GEMM column tiles x K splits
+  size_t items_off, count_off, tab_off, slot_rank_off, h_off, z_off, bytes;
 };
 DenseWs dense_ws_layout(const DenseProblem& p);
 enum { kDenseStagePlan = 0, kDenseStageShrink, kDenseStageGemm, kDenseStageCombine, kDenseNumStages };
