@@ -83,6 +83,9 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
 // fetches: a 128-row x tile is half a 256-row weight tile.)  Record:
 // {first row, rows, expert, column tile x K split}; rows = 0 marks a tile
 // past the item count.
+#ifndef MOELORA_GROUP_ITEMS
+#define MOELORA_GROUP_ITEMS 8   // work items per tile group (see above)
+#endif
 __device__ inline int4 gemm_tile_of(const int4* items, int count, int n_tiles, const int32_t* eto,
                                     int BM_tile, int E, int rows_per_item, int logical) {
   const int4 skip = make_int4(0, 0, 0, -1);
@@ -94,7 +97,7 @@ __device__ inline int4 gemm_tile_of(const int4* items, int count, int n_tiles, c
   const int rows_e = (eto[eg + 1] - eto[eg]) * BM_tile;
   const int n_e = (rows_e + rows_per_item - 1) / rows_per_item;   // the expert's items
   if (n_e <= 0) return skip;
-  const int ng = max(1, (n_e + 4) / 8);
+  const int ng = max(1, (n_e + MOELORA_GROUP_ITEMS / 2) / MOELORA_GROUP_ITEMS);
   const int gbase = n_e / ng, grem = n_e % ng;   // groups 0..grem-1 have gbase+1 items
   const int li = logical / n_tiles - first;      // an item index inside the group
   const int gj = li < grem * (gbase + 1) ? li / (gbase + 1) : grem + (li - grem * (gbase + 1)) / gbase;
