@@ -984,10 +984,119 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // latencies overlap, and its MFMAs start the accumulators.
   // Each 16-row group has its own slot; a BS-row block holds BS/16 groups, so
   // every distinct slot of the block gets its own pass with the rows of the
-  // other slots masked to zero.  The first pass of every block (usually the
-  // only one) loads its first 16-deep rank step together with the other
-  // blocks', so the whole expand waits for memory about once.
-  if (lora_here) {
+  // other slots masked to zero.
+  if constexpr (sizeof(T) == 2) {
+    // bf16: one pass per distinct slot of the wave's 16-row groups (first-seen
+    // order; usually one).  Per pass and 16-deep rank step the wave loads the
+    // B tile once for all its row blocks -- 16 rank rows x 32 columns per
+    // column block, one 16-byte load per lane -- and turns it into MFMA
+    // fragments through a wave-private scratch in the ring slot that the
+    // prologue leaves idle (the K loop refills it only after its first
+    // barrier).  Rank rows >= r and columns >= n_out are zero, never read.
+    if (lora_here) {
+      static_assert(BS == 32 && KF == 16, "bf16 expand layout");
+      constexpr int NSLOT = MB * NG;
+      constexpr int BTS = 24;   // elements per column of the scratch: 16 rank rows + pad (48 B)
+      static_assert(NWAVES * NB * 32 * BTS * (int)sizeof(T) <= STAGE_BYTES, "B scratch fits a ring slot");
+      T* bt = reinterpret_cast<T*>(lds + (STAGES - 1) * STAGE_BYTES) + wave * (NB * 32 * BTS);
+      // column block j: second pool (up columns; dense: the second output slice)?
+      auto second_of = [&](int j) -> bool {
+        return GATE_UP ? j >= NB / 2 : (DENSE && a.n_split < a.n_out && col_of(j) >= a.n_split);
+      };
+      const bool two_h = GATE_UP || (DENSE && a.HS > a.RP);   // h has a second half
+      const int qq = lane >> 2, ch = lane & 3;                 // B tile load: rank row, 8-column chunk
+      static_for<NSLOT>([&](auto C) {
+        constexpr int c = decltype(C)::value;
+        const int l = lg[c / NG][c % NG];
+        bool first = l >= 0;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2) first = first && lg[c2 / NG][c2 % NG] != l;
+        if (!first) return;
+        const int r = rg[c / NG][c % NG];
+        const int nks = (r + KF - 1) / KF;
+        // blocks holding slot l
+        bool has[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          has[i] = false;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) has[i] = has[i] || lg[i][g] == l;
+        }
+        // loads of rank step ks: B tile rows ks*16 .. ks*16+15 of slot l (this
+        // lane's 8 columns of each block), and h of this lane's row in every
+        // block holding slot l (other rows: the block's first row, zeroed later)
+        auto load_ks = [&](int ks, int4v* braw, floatx8* hg, floatx8* hu) {
+          const int q = ks * KF + qq;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const bool sec = second_of(j);
+            const T* pool = sec ? a.b_pool1 : a.b_pool0;
+            const int64_t c0 = DENSE && sec ? a.n_split : 0;
+            const int64_t width = DENSE ? (sec ? a.n_out - a.n_split : a.n_split) : a.n_out;
+            const int64_t col = col_of(j) + 8 * ch;
+            braw[j] = int4v{0, 0, 0, 0};
+            if (q < r && col < a.n_out)
+              braw[j] = *reinterpret_cast<const int4v*>(pool + (((int64_t)l * a.E + e) * a.R + q) * width + (col - c0));
+          }
+#pragma unroll
+          for (int i = 0; i < MB; ++i) {
+            const int rb = wm * WM + i * BS;
+            const bool mine = lg[i][lrow / 16] == l;
+            const float* hrow = a.h + (row0 + min(rb + (mine ? lrow : 0), nrows - 1)) * a.HS;
+            const int q0 = ks * KF + lk;
+            if (has[i]) {
+              hg[i] = *reinterpret_cast<const floatx8*>(hrow + q0);
+              hu[i] = two_h ? *reinterpret_cast<const floatx8*>(hrow + a.RP + q0) : hg[i];
+            }
+          }
+        };
+        auto proc_ks = [&](const int4v* braw, const floatx8* hg, const floatx8* hu) {
+          // transpose through the scratch: (rank row, column n of block j) at bt[(j*32 + n)*BTS + row]
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, braw[j]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) bt[(j * 32 + 8 * ch + t) * BTS + qq] = v[t];
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          frag bfr[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const frag*>(bt + (j * 32 + lrow) * BTS + lk);
+          static_for<MB>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            if (!has[i]) return;
+            const bool mine = lg[i][lrow / 16] == l;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const floatx8 hv = second_of(j) ? hu[i] : hg[i];
+              // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
+              frag hi, lo;
+#pragma unroll
+              for (int v = 0; v < 8; ++v) {
+                const float x = mine ? hv[v] : 0.0f;
+                hi[v] = (bf16_t)x;
+                lo[v] = (bf16_t)(x - (float)hi[v]);
+              }
+              acc[i][j] = B_::mma(hi, bfr[j], acc[i][j]);
+              acc[i][j] = B_::mma(lo, bfr[j], acc[i][j]);
+            }
+          });
+        };
+        // two rank steps per round, their loads issued together (one in the
+        // dense form, whose gathered rows leave no registers for a second set)
+        constexpr int PER_ROUND = DENSE ? 1 : 2;
+        for (int ks = 0; ks < nks; ks += PER_ROUND) {
+          int4v b0[NB], b1[NB];
+          floatx8 hg0[MB], hu0[MB], hg1[MB], hu1[MB];
+          load_ks(ks, b0, hg0, hu0);
+          const bool two = PER_ROUND == 2 && ks + 1 < nks;
+          if (two) load_ks(ks + 1, b1, hg1, hu1);
+          proc_ks(b0, hg0, hu0);
+          if (two) proc_ks(b1, hg1, hu1);
+        }
+      });
+    }
+  } else if (lora_here) {
     constexpr int MAXKS = 64 / KF;   // RP <= 64
     // dense mode: column block j belongs to the second output slice
     auto dense_second = [&](int j) -> bool {
