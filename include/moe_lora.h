@@ -181,6 +181,9 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
  *                combine result without the final rounding to bf16).
  * num_loras == 0 (pools NULL) runs the plain MoE layer.  H and I must be
  * multiples of 64, R <= 64, top_k <= num_experts.
+ * x, the expert weights, the six pools, y and the workspace must be 16-byte
+ * aligned (the kernels read and write them in 16-byte units); a misaligned
+ * pointer is MOE_LORA_ERR_INVALID.
  *
  * FP8 expert weights (the fields after out_dtype; a caller whose struct_size
  * ends at out_dtype gets weights in `dtype`):
@@ -282,7 +285,8 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
  *   lora_ranks   [L] int32, scaling [L] float32: as for the MoE layer.
  *   the align outputs, workspace (>= moe_lora_dense_workspace_bytes) and
  *   y            [T, N0 + N1] out  overwritten, in out_dtype (dtype or F32).
- * H, N0 and N1 must be multiples of 64 (N0 > 0, N1 >= 0), R <= 64.  Errors and
+ * H, N0 and N1 must be multiples of 64 (N0 > 0, N1 >= 0), R <= 64.  x, w, the
+ * four pools, y and the workspace must be 16-byte aligned.  Errors and
  * ownership as for moe_lora_forward.
  */
 typedef struct moe_lora_dense_args {

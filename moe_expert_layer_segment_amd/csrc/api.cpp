@@ -97,6 +97,9 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
                                  static_cast<hipStream_t>(stream)));
 }
 
+// the kernels move activations, weights, pools and outputs in 16-byte units
+static bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
 static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool check_ptrs) {
   // the fields up to out_dtype are required; the fp8 weight fields are read
   // when struct_size covers them
@@ -119,6 +122,12 @@ static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool ch
       return MOE_LORA_ERR_INVALID;
     if (a->num_loras > 0 && (!a->a_gate || !a->a_up || !a->b_gate || !a->b_up || !a->a_down ||
                              !a->b_down || !a->lora_ranks || !a->scaling))
+      return MOE_LORA_ERR_INVALID;
+    if (misaligned(a->x) || misaligned(a->w_gate_up) || misaligned(a->w_down) || misaligned(a->y) ||
+        misaligned(a->workspace))
+      return MOE_LORA_ERR_INVALID;
+    if (a->num_loras > 0 && (misaligned(a->a_gate) || misaligned(a->a_up) || misaligned(a->b_gate) ||
+                             misaligned(a->b_up) || misaligned(a->a_down) || misaligned(a->b_down)))
       return MOE_LORA_ERR_INVALID;
   }
   p->dtype = a->dtype;
@@ -195,6 +204,10 @@ static int to_dense(const moe_lora_dense_args* a, DenseProblem* p, bool check_pt
       return MOE_LORA_ERR_INVALID;
     if (a->num_loras > 0 && (!a->a0 || !a->b0 || !a->lora_ranks || !a->scaling ||
                              (a->out1 > 0 && (!a->a1 || !a->b1))))
+      return MOE_LORA_ERR_INVALID;
+    if (misaligned(a->x) || misaligned(a->w) || misaligned(a->y) || misaligned(a->workspace) ||
+        (a->num_loras > 0 && (misaligned(a->a0) || misaligned(a->b0) || misaligned(a->a1) ||
+                              misaligned(a->b1))))
       return MOE_LORA_ERR_INVALID;
   }
   p->dtype = a->dtype;

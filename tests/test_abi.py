@@ -147,6 +147,10 @@ def test_forward_validation_codes():
     assert call(block_m=24) == binding.ERR_INVALID
     assert call(x=None) == binding.ERR_INVALID
     assert call(a_down=None) == binding.ERR_INVALID
+    # 16-byte units: a misaligned activation, weight, pool, output or workspace is refused
+    for n in ("x", "w_gate_up", "w_down", "b_gate", "b_down", "a_up", "y", "workspace"):
+        assert call(**{n: 0x1008}) == binding.ERR_INVALID, n
+    assert call(num_loras=0, b_down=0x1002) == binding.ERR_WORKSPACE   # pools unused
     assert call() == binding.ERR_WORKSPACE           # 1-byte workspace
     assert call(num_loras=0, a_gate=None) == binding.ERR_WORKSPACE  # plain MoE needs no pools
     ws = lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
@@ -221,6 +225,8 @@ def test_dense_validation_codes():
     assert call(block_m=24) == binding.ERR_INVALID
     assert call(w=None) == binding.ERR_INVALID
     assert call(b1=None) == binding.ERR_INVALID
+    for n in ("x", "w", "b0", "a1", "y", "workspace"):
+        assert call(**{n: 0x1004}) == binding.ERR_INVALID, n   # 16-byte units
     assert call(out1=0, a1=None, b1=None) == binding.ERR_WORKSPACE   # one slice needs no second pool
     assert call(num_loras=0, a0=None, b0=None, a1=None, b1=None) == binding.ERR_WORKSPACE
     assert call(num_tokens=0) == binding.OK
