@@ -142,11 +142,16 @@ def copy_calibration(mib):
 
 class HipEvents:
     """Raw hipEvent_t handles through libamdhip64 (recorded by the library on
-    the stream its kernels run on)."""
+    the stream its kernels run on).  Created without the system-scope fence: a
+    default event record writes back and invalidates the caches, which idles
+    the GPU for microseconds and starts the next kernel with a cold L2; these
+    events only time work."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -155,8 +160,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
 
@@ -169,6 +174,45 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def timed_steps(args, torch, hip, step, stages, kernel):
+    """Time args.steps steps between two events on the launch stream.  Inside
+    the timed region only the dominant kernel is bracketed by HIP events (its
+    live duration for the roofline): every event recorded between kernels
+    leaves the GPU idle for several microseconds, which a marker at each stage
+    boundary would add to the step.  The per-stage breakdown comes from
+    further, untimed steps with an event pair around every stage.
+    Returns (ms per step, kernel ms, {stage: ms})."""
+    nst = len(stages)
+    ki = stages.index(kernel)
+    ev = []
+    for _ in range(args.steps):
+        pair = hip.create(2)
+        e = [None] * (2 * nst)
+        e[2 * ki], e[2 * ki + 1] = pair
+        ev.append(e)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for st in range(args.steps):
+        step(ev[st])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    k_ms = float(np.mean([hip.elapsed_ms(e[2 * ki], e[2 * ki + 1]) for e in ev]))
+    for e in ev:
+        hip.destroy([e[2 * ki], e[2 * ki + 1]])
+    nb = max(1, min(args.steps, 10))
+    evb = [hip.create(2 * nst) for _ in range(nb)]
+    for st in range(nb):
+        step(evb[st])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evb]))
+                for i, name in enumerate(stages)}
+    for e in evb:
+        hip.destroy(e)
+    return ms, k_ms, stage_ms
 
 
 def counts(spec, meta):
@@ -297,7 +341,6 @@ def dense_main(args, torch, binding, workloads, dev):
         inp["x"], inp["w"], N0, al, inp["lora_ranks"], inp["scaling"], pools), dtype=torch.uint8,
         device=dev)
     hip = HipEvents()
-    nst = len(binding.DENSE_STAGES)
 
     def step(events=None):
         binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
@@ -312,19 +355,7 @@ def dense_main(args, torch, binding, workloads, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [hip.create(2 * nst) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for st in range(args.steps):
-        step(ev[st])
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in ev]))
-                for i, name in enumerate(binding.DENSE_STAGES)}
-    for e in ev:
-        hip.destroy(e)
+    ms, g_ms, stage_ms = timed_steps(args, torch, hip, step, binding.DENSE_STAGES, "gemm")
 
     m = inp["meta"]
     ranks = np.asarray(m["lora_ranks"])
@@ -335,7 +366,6 @@ def dense_main(args, torch, binding, workloads, dev):
     gemm_flops = 2.0 * T * H * N + 2.0 * float(np.sum(r_tok)) * N
     total_flops = gemm_flops + 2.0 * float(np.sum(r_tok)) * H * (2 if N1 > 0 else 1)
     gemm_bytes = N * H * esz + T * H * esz + 4.0 * T * N
-    g_ms = stage_ms["gemm"]
     peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_FP32_TFLOPS
     if gemm_flops / gemm_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         a = gemm_flops / (g_ms * 1e-3) / 1e12
@@ -435,7 +465,6 @@ def main():
         inp["lora_ranks"], inp["scaling"], pools, w_scales), dtype=torch.uint8, device=dev)
 
     hip = HipEvents()
-    nst = len(binding.FORWARD_STAGES)
 
     def step(events=None):
         binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
@@ -452,21 +481,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    ev = [hip.create(2 * nst) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(ev[s])
-    stop.record()
-    torch.cuda.synchronize()
+    ms, gu_ms, stage_ms = timed_steps(args, torch, hip, step, binding.FORWARD_STAGES, "gate_up_gemm")
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
-    stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in ev]))
-                for i, name in enumerate(binding.FORWARD_STAGES)}
-    for e in ev:
-        hip.destroy(e)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
@@ -486,7 +503,6 @@ def main():
     router_ms = r_start.elapsed_time(r_stop) / 20
 
     c = counts(spec, inp["meta"])
-    gu_ms = stage_ms["gate_up_gemm"]
     achieved = c["gate_up_flops"] / (gu_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_FP32_TFLOPS
     traffic = None
