@@ -18,7 +18,7 @@
 
 namespace moelora {
 
-static constexpr int kAlignSteps = 8;       // 64-pair steps per wave in the count kernel
+static constexpr int kAlignSteps = 8;       // at most this many 64-pair steps per wave in the count kernel
 static constexpr int kScanThreads = 1024;
 static constexpr int kScatterThreads = 256;
 
@@ -28,11 +28,21 @@ int align_waves_for_keys(int64_t K) {
   return 1;
 }
 
-int64_t align_chunk_pairs(int64_t K) { return (int64_t)align_waves_for_keys(K) * kAlignSteps * 64; }
+// 64-pair steps per wave: as many as keep the chunk count near 16, so a
+// small batch spreads over several workgroups instead of walking its pairs
+// step by step in one (the scan's cost grows with chunks x keys)
+int align_steps(int64_t P, int64_t K) {
+  const int64_t per_step = (int64_t)align_waves_for_keys(K) * 64;
+  return (int)std::min<int64_t>(kAlignSteps, std::max<int64_t>(1, ceil_div(P, per_step * 16)));
+}
+
+int64_t align_chunk_pairs(int64_t P, int64_t K) {
+  return (int64_t)align_waves_for_keys(K) * align_steps(P, K) * 64;
+}
 
 AlignWs align_ws_layout(int64_t P, int64_t K) {
   AlignWs w;
-  int64_t ch = align_chunk_pairs(K);
+  int64_t ch = align_chunk_pairs(P, K);
   w.nchunks = P > 0 ? ceil_div(P, ch) : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
@@ -56,7 +66,7 @@ __device__ inline int pair_key(int p, int k, int E, int L, const int32_t* __rest
 }
 
 __global__ void __launch_bounds__(256)
-align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves,
+align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves, int steps,
                    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ mapping,
                    const int32_t* __restrict__ enabled, int32_t* __restrict__ ws_rank,
                    int32_t* __restrict__ ws_cnt) {
@@ -66,8 +76,8 @@ align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves,
   for (int i = lane; i < K; i += 64) h[i] = 0;
 
   const int chunk = blockIdx.x;
-  const int64_t chunk_pairs = (int64_t)waves * kAlignSteps * 64;
-  const int64_t wbase = chunk * chunk_pairs + (int64_t)wave * kAlignSteps * 64;
+  const int64_t chunk_pairs = (int64_t)waves * steps * 64;
+  const int64_t wbase = chunk * chunk_pairs + (int64_t)wave * steps * 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
 
   int keys[kAlignSteps], ranks[kAlignSteps];
@@ -75,7 +85,7 @@ align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves,
   for (int s = 0; s < kAlignSteps; ++s) {
     const int64_t p = wbase + s * 64 + lane;
     int key = -1;
-    if (p < P) key = pair_key((int)p, k, E, L, topk_ids, mapping, enabled);
+    if (s < steps && p < P) key = pair_key((int)p, k, E, L, topk_ids, mapping, enabled);
     const bool valid = key >= 0;
     // lanes holding the same key: AND of per-bit ballots
     uint64_t m = __ballot(valid);
@@ -109,7 +119,7 @@ align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves,
 #pragma unroll
   for (int s = 0; s < kAlignSteps; ++s) {
     const int64_t p = wbase + s * 64 + lane;
-    if (p < P && keys[s] >= 0) ws_rank[p] = ranks[s] + h[keys[s]];
+    if (s < steps && p < P && keys[s] >= 0) ws_rank[p] = ranks[s] + h[keys[s]];
   }
 }
 
@@ -232,8 +242,8 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
   const size_t lds = (size_t)waves * K * sizeof(uint16_t);
 
   hipLaunchKernelGGL(align_count_kernel, dim3((unsigned)w.nchunks), dim3(64 * waves), lds, stream,
-                     (int)P, k, E, L, (int)K, key_bits, waves, topk_ids, mapping, enabled, ws_rank,
-                     ws_cnt);
+                     (int)P, k, E, L, (int)K, key_bits, waves, align_steps(P, K), topk_ids, mapping,
+                     enabled, ws_rank, ws_cnt);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, (int)w.nchunks,
                      (int)K, E, L, BM, ws_cnt, ws_bstart, ws_btotal, expert_tile_offsets,
                      num_rows_padded);
@@ -242,7 +252,7 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
   if (n > 0) {
     hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)ceil_div(n, kScatterThreads)),
                        dim3(kScatterThreads), 0, stream, (int)P, k, E, L, (int)K, BM, cap,
-                       align_chunk_pairs(K), topk_ids, mapping, enabled, ws_rank, ws_cnt,
+                       align_chunk_pairs(P, K), topk_ids, mapping, enabled, ws_rank, ws_cnt,
                        ws_bstart, ws_btotal, sorted_ids, tile_expert, tile_lora);
   }
   return hipGetLastError();

@@ -14,7 +14,7 @@ struct AlignWs {
   size_t rank_off, cnt_off, bstart_off, btotal_off, bytes;
 };
 AlignWs align_ws_layout(int64_t num_pairs, int64_t num_keys);
-int64_t align_chunk_pairs(int64_t num_keys);
+int64_t align_chunk_pairs(int64_t num_pairs, int64_t num_keys);
 
 // rows of the align outputs: P + min(P, E*(L+1)) * (BM - 1), rounded up to BM
 inline int64_t align_capacity(int64_t P, int64_t E, int64_t L, int64_t BM) {
