@@ -973,9 +973,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       compute(s % STAGES, -1, 0, s);
     }
   };
-  // the ring's first STAGES-1 stages
+  // the ring's first STAGES-1 stages: all but the last before the expand, the
+  // last right after it (the expand waits for every load issued before its
+  // own, the inline-asm DMA included, so that stage then stays in flight
+  // into the K loop)
+  constexpr int PRE = STAGES > 2 ? STAGES - 2 : 1;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
+  for (int st = 0; st < PRE; ++st)
     if (st < nk) issue_stage(st, st);
   if constexpr (WF8) fill_scales();
 
@@ -1202,6 +1206,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     });
   }
 
+#pragma unroll
+  for (int st = PRE; st < STAGES - 1; ++st)
+    if (st < nk) issue_stage(st, st);
   if (wm * WM + WM <= nrows)
     main_loop(std::true_type{});
   else
