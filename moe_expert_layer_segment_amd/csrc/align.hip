@@ -157,32 +157,73 @@ align_scan_kernel(int nchunks, int K, int E, int L, int BM, int32_t* __restrict_
   __shared__ int lds_waves[kScanThreads / 64 + 1];
   const int kpt = (K + kScanThreads - 1) / kScanThreads;
   const int k0 = min(K, (int)threadIdx.x * kpt), k1 = min(K, k0 + kpt);
+  // A thread's keys k0..k1-1 are scanned over the chunks in place.  Loads and
+  // stores of one array keep their program order, so a key-by-key loop waits
+  // for memory once per key; when the thread's block of counts is small
+  // (decode-sized batches) it is read into registers first, all at once.
+  constexpr int KB = 8, CB = 8;
+  const bool small = kpt <= KB && nchunks <= CB;   // uniform
+  int v[KB][CB], tot[KB];
   int mine = 0;
-  for (int key = k0; key < k1; ++key) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int64_t idx = (int64_t)c * K + key;
-      int v = ws_cnt[idx];
-      ws_cnt[idx] = run;
-      run += v;
+  if (small) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+        v[kk][c] = (k0 + kk < k1 && c < nchunks) ? ws_cnt[(int64_t)c * K + k0 + kk] : 0;
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      int run = 0;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int x = v[kk][c];
+        v[kk][c] = run;
+        run += x;
+      }
+      tot[kk] = run;
+      if (k0 + kk < k1) mine += (int)round_up(run, BM);
     }
-    ws_btotal[key] = run;
-    mine += (int)round_up(run, BM);
+  } else {
+    for (int key = k0; key < k1; ++key) {
+      int run = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        int64_t idx = (int64_t)c * K + key;
+        int x = ws_cnt[idx];
+        ws_cnt[idx] = run;
+        run += x;
+      }
+      ws_btotal[key] = run;
+      mine += (int)round_up(run, BM);
+    }
   }
   int total = 0;
   int start = block_exclusive_scan(mine, lds_waves, &total);
-  for (int key = k0; key < k1; ++key) {
-    ws_bstart[key] = start;
-    for (int c = 0; c < nchunks; ++c) ws_cnt[(int64_t)c * K + key] += start;
-    start += (int)round_up(ws_btotal[key], BM);
+  if (small) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int key = k0 + kk;
+      if (key >= k1) continue;
+      ws_btotal[key] = tot[kk];
+      ws_bstart[key] = start;
+      if (key % (L + 1) == 0) expert_tile_offsets[key / (L + 1)] = start / BM;   // the expert's first key
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+        if (c < nchunks) ws_cnt[(int64_t)c * K + key] = v[kk][c] + start;
+      start += (int)round_up(tot[kk], BM);
+    }
+  } else {
+    for (int key = k0; key < k1; ++key) {
+      ws_bstart[key] = start;
+      if (key % (L + 1) == 0) expert_tile_offsets[key / (L + 1)] = start / BM;   // the expert's first key
+      for (int c = 0; c < nchunks; ++c) ws_cnt[(int64_t)c * K + key] += start;
+      start += (int)round_up(ws_btotal[key], BM);
+    }
   }
   if (threadIdx.x == 0) {
     ws_bstart[K] = total;
     num_rows_padded[0] = total;
+    expert_tile_offsets[E] = total / BM;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += kScanThreads)
-    expert_tile_offsets[e] = (e < E ? ws_bstart[e * (L + 1)] : total) / BM;
 }
 
 __global__ void __launch_bounds__(kScatterThreads)

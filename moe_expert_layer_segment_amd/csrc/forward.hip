@@ -261,14 +261,14 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
 }
 
 // The same shrink with the pool rows shared through LDS: a workgroup takes
-// 4 consecutive 16-row groups (one per wave) of one K split; when they belong
+// NW consecutive 16-row groups (one per wave) of one K split; when they belong
 // to one (expert, slot) bucket -- the common case -- the bucket's pool rows
 // are loaded once per 128-deep K chunk into LDS by the whole workgroup
 // (double-buffered, register-staged) and each wave multiplies its own rows
 // against them.  A wave whose group has another slot reads its pool rows from
 // global memory instead.  Pool rows past the slot's rank are never read.
-template <typename T, int NPOOL>
-__global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
+template <typename T, int NPOOL, int NW>
+__global__ void __launch_bounds__(64 * NW) shrink4_kernel(ShrinkArgs<T> a) {
   typedef Elt<T> E_;
   typedef typename E_::frag frag;
   constexpr int NQB = 4;                            // up to 64 rank columns per pool
@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
   T* const pool_lds = reinterpret_cast<T*>(shrink4_lds);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t nrp = a.num_rows_padded[0];
-  const int64_t g0 = (int64_t)blockIdx.x * 4;       // the workgroup's first group
+  const int64_t g0 = (int64_t)blockIdx.x * NW;      // the workgroup's first group
   if (g0 * 16 >= nrp) return;
   const int64_t k_begin = (int64_t)blockIdx.y * a.kchunk;
   const int64_t k_end = min(a.K, k_begin + a.kchunk);
@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
   };
   // the shared bucket: the first group's with a positive rank
   int sl = -1, se = -1, sr = 0;
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     int l, e, r;
     if (group_key(w, l, e, r) && r > 0) { sl = l; se = e; sr = r; break; }
   }
@@ -353,12 +353,13 @@ __global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
   const int RPL = a.RP;                             // LDS rows per pool
   const int64_t buf_elems = (int64_t)NPOOL * RPL * ROWEL;
   const int PIECES = NPOOL * RPL * CPQ;
-  constexpr int PER_THREAD = (NPOOL * 64 * CPQ + 255) / 256;  // RP <= 64
+  constexpr int NT = 64 * NW;                        // threads
+  constexpr int PER_THREAD = (NPOOL * 64 * CPQ + NT - 1) / NT;  // RP <= 64
   int4v stage[PER_THREAD];
   auto load_chunk = [&](int64_t kc0, int valid) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = threadIdx.x + i * 256;
+      const int c = threadIdx.x + i * NT;
       const int pi = c / (RPL * CPQ), q = (c / CPQ) % RPL, pc = c % CPQ;
       const bool ok = c < PIECES && q < sr && pc * (16 / (int)sizeof(T)) < valid;
       const T* pool = pi == 0 ? a.pool0 : a.pool1;
@@ -370,7 +371,7 @@ __global__ void __launch_bounds__(256) shrink4_kernel(ShrinkArgs<T> a) {
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = threadIdx.x + i * 256;
+      const int c = threadIdx.x + i * NT;
       if (c >= PIECES) continue;
       const int pi = c / (RPL * CPQ), q = (c / CPQ) % RPL, pc = c % CPQ;
       *reinterpret_cast<int4v*>(&pool_lds[buf * buf_elems + (pi * RPL + q) * ROWEL +
@@ -1416,6 +1417,12 @@ static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : 
 #define MOELORA_SHRINK4_MIN_P 65536
 #endif
 
+// waves (16-row groups) per workgroup of the LDS-shared shrink
+#ifndef MOELORA_SHRINK_SHARED_WAVES
+#define MOELORA_SHRINK_SHARED_WAVES 4
+#endif
+static constexpr int kShrinkSharedWaves = MOELORA_SHRINK_SHARED_WAVES;
+
 static bool use_shrink4(int64_t P, int64_t E, int64_t L) {
   return L > 0 && P >= (int64_t)MOELORA_SHRINK4_MIN_P && P >= (int64_t)MOELORA_SHRINK4_MIN_ROWS * E * L;
 }
@@ -1424,8 +1431,9 @@ template <typename T, int NPOOL>
 static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bool shared,
                           hipStream_t stream) {
   if (shared)  // two LDS buffers of NPOOL * RP pool rows of 256 bytes
-    hipLaunchKernelGGL((shrink4_kernel<T, NPOOL>), dim3((unsigned)ceil_div(groups, 4), (unsigned)splits),
-                       dim3(256), (size_t)2 * NPOOL * s.RP * 256, stream, s);
+    hipLaunchKernelGGL((shrink4_kernel<T, NPOOL, kShrinkSharedWaves>),
+                       dim3((unsigned)ceil_div(groups, kShrinkSharedWaves), (unsigned)splits),
+                       dim3(64 * kShrinkSharedWaves), (size_t)2 * NPOOL * s.RP * 256, stream, s);
   else
     hipLaunchKernelGGL((shrink_kernel<T, NPOOL>), dim3((unsigned)groups, (unsigned)splits),
                        dim3(256), 0, stream, s);
@@ -1435,7 +1443,7 @@ static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bo
 // each split at least 512 deep
 static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared) {
   const int64_t groups = P / 16 + 1;
-  const int64_t wgs = shared ? ceil_div(groups, 4) : groups;
+  const int64_t wgs = shared ? ceil_div(groups, kShrinkSharedWaves) : groups;
   int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(1024, wgs)));
   s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
   return round_up(ceil_div(K, s), 128);
