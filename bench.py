@@ -428,8 +428,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the layer is TP=1 on a single MI355X and this build "
-              "has no multi-GPU path (see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs at TP=1 on a single MI355X; there is "
+              "no multi-GPU path (the per-rank kernels run at their shard shapes with "
+              "--config c1_tp8, c4p_ep8 or c4d_ep8).", file=sys.stderr)
         sys.exit(2)
 
     import torch
