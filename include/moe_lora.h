@@ -2,7 +2,7 @@
  * moe_lora.h -- C ABI of the MI355X (gfx950) MoE expert layer with per-request
  * LoRA deltas.
  *
- * The layer (SGLang PR #14105 page, "LoRA on MoE expert layers", section
+ * The layer (SGLang PR #14105 page, on LoRA for MoE expert layers, section
  * 实现拆解, the layer formula) computes, for every token t with top-k experts
  * e_j and router weights w_j, and the token's adapter slot l:
  *
@@ -11,7 +11,7 @@
  *
  * with LoRA factors taken from 4-D pools [num_loras, num_experts, rank, dim]
  * (same page, same section) and the slot picked per token from request
- * segments (SGLang PR #24160 page, "shared MoE LoRA batch info", sections
+ * segments (SGLang PR #24160 page, on sharing the MoE LoRA batch info, sections
  * 实现拆解 and 关键源码片段).
  *
  * Three calls, plus the router step before them:
@@ -263,8 +263,8 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
                             void* const* events);
 
 /*
- * Dense projection with per-request LoRA and a two-slice output ("LoRA on a
- * fused projection whose outputs have unequal sizes": the SGLang PR #22323
+ * Dense projection with per-request LoRA and a two-slice output (LoRA on a
+ * fused projection with outputs of unequal sizes: the SGLang PR #22323
  * page, sections 功能与动机 and 实现拆解 item 2 -- the fused q_a_proj +
  * kv_a_proj_with_mqa projection of MLA, whose LoRA B is split in two and
  * applied per output part).  For token t in a request using slot l:

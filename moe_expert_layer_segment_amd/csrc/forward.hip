@@ -1,5 +1,5 @@
-// The MoE-LoRA layer forward on gfx950 (SGLang PR #14105 page, "LoRA on MoE
-// expert layers", section 实现拆解: y = (W_down + s B_d A_d)[SiLU((W_gate + s B_g A_g)x)
+// The MoE-LoRA layer forward on gfx950 (SGLang PR #14105 page, on LoRA for MoE
+// expert layers, section 实现拆解: y = (W_down + s B_d A_d)[SiLU((W_gate + s B_g A_g)x)
 // * ((W_up + s B_u A_u)x)], summed over the top-k experts with the router weights).
 //
 // Launch sequence on one stream, no host synchronisation:

@@ -1,5 +1,5 @@
-// Per-batch MoE-LoRA metadata (SGLang PR #24160 page, "shared MoE LoRA batch
-// info", section 实现拆解 items 1-3): token_lora_mapping expands each request's
+// Per-batch MoE-LoRA metadata (SGLang PR #24160 page, on sharing the MoE LoRA
+// batch info, section 实现拆解 items 1-3): token_lora_mapping expands each request's
 // slot over its segment; adapter_enabled marks slots named by some request whose
 // rank is > 0 (-1 entries are masked before the scatter, as the page's review
 // section asks).

@@ -6,12 +6,12 @@ the HIP path and imports nothing from it.
 
 Sources (the pages are summaries of SGLang pull requests):
 
-* "SGLang PR #14105 -- LoRA on MoE expert layers", section 实现拆解: the layer
+* the SGLang PR #14105 page (LoRA for MoE expert layers), section 实现拆解: the layer
   formula y = (W_down + (alpha/r) B_d A_d)[SiLU((W_gate + (alpha/r) B_g A_g) x)
   * ((W_up + (alpha/r) B_u A_u) x)], LoRA inserted after gate_up and before
   down; the align step sorts tokens by adapter and expert id; the LoRA pool is
   4-D [num_loras, num_experts, rank, dim].
-* "SGLang PR #24160 -- shared MoE LoRA batch info", sections 实现拆解 and
+* the SGLang PR #24160 page (sharing the MoE LoRA batch info), sections 实现拆解 and
   关键源码片段: per-batch metadata (seg_indptr, req_to_lora, adapter_enabled,
   token_lora_mapping with -1 = no adapter), the repeat_interleave / scatter
   closed forms of the unit test, the under-coverage assertion; section 评论区精华:
