@@ -1439,13 +1439,19 @@ static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bo
                        dim3(256), 0, stream, s);
 }
 
-// K elements per split: enough splits for about 1024 workgroups of 4 waves,
-// each split at least 512 deep
+// K elements per split: enough splits for about MOELORA_SHRINK_WGS workgroups
+// of 4 waves, each split at least MOELORA_SHRINK_MIN_K deep
+#ifndef MOELORA_SHRINK_WGS
+#define MOELORA_SHRINK_WGS 1024
+#endif
+#ifndef MOELORA_SHRINK_MIN_K
+#define MOELORA_SHRINK_MIN_K 512
+#endif
 static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared) {
   const int64_t groups = P / 16 + 1;
   const int64_t wgs = shared ? ceil_div(groups, kShrinkSharedWaves) : groups;
-  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(1024, wgs)));
-  s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
+  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(MOELORA_SHRINK_WGS, wgs)));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / MOELORA_SHRINK_MIN_K));
   return round_up(ceil_div(K, s), 128);
 }
 static int shrink_splits(int64_t P, int64_t K, bool shared) {
