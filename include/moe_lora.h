@@ -246,7 +246,7 @@ int moe_lora_forward(const moe_lora_forward_args* args, void* stream);
 
 /*
  * Number of kernel stages of moe_lora_forward, in launch order: 0 plan (work
- * items), 1 gate/up LoRA shrink, 2 gate_up GEMM (+LoRA expand, SiLU*mul),
+ * items and tile tables), 1 gate/up LoRA shrink, 2 gate_up GEMM (+LoRA expand, SiLU*mul),
  * 3 down LoRA shrink, 4 down GEMM (+LoRA expand, router weight), 5 top-k combine.
  */
 #define MOE_LORA_FORWARD_STAGES 6
@@ -255,8 +255,12 @@ int moe_lora_forward(const moe_lora_forward_args* args, void* stream);
  * moe_lora_forward_events -- moe_lora_forward for measurement: additionally
  * records the caller's hipEvent_t handles on `stream`, events[2s] before and
  * events[2s+1] after stage s (s < MOE_LORA_FORWARD_STAGES; NULL entries are
- * skipped; a stage that launches nothing gets two adjacent records).  Adds no
- * synchronisation; results are identical to moe_lora_forward.  The caller owns
+ * skipped; a stage that launches nothing gets two adjacent records).  The two
+ * GEMM stages (2 and 4), one kernel each, hand their pair to the kernel launch
+ * itself (hipExtLaunchKernel: the dispatch records the kernel's start and end),
+ * so timing them puts no marker between kernels; the other stages' events are
+ * recorded with hipEventRecord.  Adds no synchronisation; results are
+ * identical to moe_lora_forward.  The caller owns
  * the events and reads them with hipEventElapsedTime after synchronising.
  */
 int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
@@ -319,7 +323,9 @@ int moe_lora_dense_forward(const moe_lora_dense_args* args, void* stream);
 
 /* moe_lora_dense_forward plus caller-owned HIP events recorded around its four
  * kernel stages (plan, shrink, GEMM, combine): events[2s] before and
- * events[2s+1] after stage s; NULL entries are skipped.  Measurement only. */
+ * events[2s+1] after stage s; NULL entries are skipped; the GEMM stage's pair
+ * is recorded by its kernel launch, as in moe_lora_forward_events.
+ * Measurement only. */
 int moe_lora_dense_forward_events(const moe_lora_dense_args* args, void* stream,
                                   void* const* events);
 

@@ -14,6 +14,8 @@
 //   down     -- grouped MFMA GEMM act * W_down^T + h_d B_d, times the router weight,
 //               written to z in pair order (fp32).
 //   combine  -- y[t] = sum_j z[t*k + j] for j = 0..k-1 in order (fp32), cast to dtype.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1497,7 +1499,9 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
 template <typename T>
 static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
                              hipEvent_t* events) {
-  // optional measurement: events[2s] / events[2s+1] bracket stage s
+  // optional measurement: events[2s] / events[2s+1] bracket stage s; the
+  // single-kernel GEMM stages hand theirs to the launch itself (the dispatch
+  // records them: no marker packets, which idle the GPU between kernels)
   auto mark = [&](int idx) {
     if (events && events[idx]) (void)hipEventRecord(events[idx], stream);
   };
@@ -1598,22 +1602,21 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.act = act;
     a.tile_ctr = count + 4;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
-    mark(2 * kStageGateUp);
+    hipEvent_t ev0 = events ? events[2 * kStageGateUp] : nullptr, ev1 = events ? events[2 * kStageGateUp + 1] : nullptr;
     if constexpr (kBf16) {
       if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
-        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
       } else if (fp8w) {
         typedef Fp8DecodeCfg F;
-        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
       }
     }
     if (!fp8w)
-      hipLaunchKernelGGL((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
-                         dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
-    mark(2 * kStageGateUp + 1);
+      hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
+                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
   }
   mark(2 * kStageShrinkA);
   if (lora && groups > 0) {
@@ -1664,22 +1667,21 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.z = z;
     a.tile_ctr = count + 12;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
-    mark(2 * kStageDown);
+    hipEvent_t ev0 = events ? events[2 * kStageDown] : nullptr, ev1 = events ? events[2 * kStageDown + 1] : nullptr;
     if constexpr (kBf16) {
       if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
-        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
       } else if (fp8w) {
         typedef Fp8DecodeCfg F;
-        hipLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, a);
+        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
       }
     }
     if (!fp8w)
-      hipLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
-                         dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
-    mark(2 * kStageDown + 1);
+      hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
+                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
   }
   mark(2 * kStageCombine);
   if (P > 0) {
@@ -1800,7 +1802,7 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
   }
   mark(2 * kDenseStageShrink + 1);
 
-  mark(2 * kDenseStageGemm);
+  if (P == 0) mark(2 * kDenseStageGemm);
   if (P > 0) {
     GemmArgs<T> a{};
     a.items = items;
@@ -1835,10 +1837,13 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     a.z = z;
     a.tile_ctr = count + 4;
     const int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
-    hipLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false, true>),
-                       dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, a);
+    // the stage's events, when given, are taken by the launch itself
+    hipEvent_t ev0 = events ? events[2 * kDenseStageGemm] : nullptr;
+    hipEvent_t ev1 = events ? events[2 * kDenseStageGemm + 1] : nullptr;
+    hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false, true>),
+                          dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
   }
-  mark(2 * kDenseStageGemm + 1);
+  if (P == 0) mark(2 * kDenseStageGemm + 1);
 
   mark(2 * kDenseStageCombine);
   if (P > 0) {
