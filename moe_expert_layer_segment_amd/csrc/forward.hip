@@ -1442,22 +1442,25 @@ static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bo
 }
 
 // K elements per split: enough splits for about MOELORA_SHRINK_WGS workgroups
-// of 4 waves, each split at least MOELORA_SHRINK_MIN_K deep
+// of 4 waves, each split at least npool * MOELORA_SHRINK_MIN_K deep (a split
+// of the layer's two-pool gate/up shrink carries twice the pool rows per K
+// element, and measured faster at twice the depth; the one-pool down shrink
+// and the dense projection's shrink are kept at the single depth)
 #ifndef MOELORA_SHRINK_WGS
 #define MOELORA_SHRINK_WGS 1024
 #endif
 #ifndef MOELORA_SHRINK_MIN_K
 #define MOELORA_SHRINK_MIN_K 512
 #endif
-static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared) {
+static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared, int npool) {
   const int64_t groups = P / 16 + 1;
   const int64_t wgs = shared ? ceil_div(groups, kShrinkSharedWaves) : groups;
   int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(MOELORA_SHRINK_WGS, wgs)));
-  s = std::min<int64_t>(s, std::max<int64_t>(1, K / MOELORA_SHRINK_MIN_K));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / ((int64_t)npool * MOELORA_SHRINK_MIN_K)));
   return round_up(ceil_div(K, s), 128);
 }
-static int shrink_splits(int64_t P, int64_t K, bool shared) {
-  return (int)ceil_div(K, shrink_kchunk(P, K, shared));
+static int shrink_splits(int64_t P, int64_t K, bool shared, int npool) {
+  return (int)ceil_div(K, shrink_kchunk(P, K, shared, npool));
 }
 
 ForwardWs forward_ws_layout(const ForwardProblem& p) {
@@ -1474,8 +1477,8 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.items_off = take(sizeof(int4) * (size_t)w.max_items);
   w.count_off = take(sizeof(int32_t) * 20);   // item count, then 2 x 8 tile counters
   w.shrink4 = use_shrink4(P, p.E, p.L);
-  w.split_gu = shrink_splits(P, p.H, w.shrink4);
-  w.split_d = shrink_splits(P, p.I, w.shrink4);
+  w.split_gu = shrink_splits(P, p.H, w.shrink4, 2);
+  w.split_d = shrink_splits(P, p.I, w.shrink4, 1);
   w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
                                 : down_ksplit<float>(P, p.E, p.H, p.I, false);
   if (p.dtype == 1) {
@@ -1556,7 +1559,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hgu;
     s.cap = w.cap;
-    s.kchunk = shrink_kchunk(P, p.H, w.shrink4);
+    s.kchunk = shrink_kchunk(P, p.H, w.shrink4, 2);
     s.split_stride = w.cap * 2 * w.RP;
     launch_shrink<T, 2>(s, groups, w.split_gu, w.shrink4, stream);
     if (w.split_gu > 1)
@@ -1637,7 +1640,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.scaling = p.scaling;
     s.h = hd;
     s.cap = w.cap;
-    s.kchunk = shrink_kchunk(P, p.I, w.shrink4);
+    s.kchunk = shrink_kchunk(P, p.I, w.shrink4, 1);
     s.split_stride = w.cap * w.RP;
     launch_shrink<T, 1>(s, groups, w.split_d, w.shrink4, stream);
     if (w.split_d > 1)
@@ -1723,7 +1726,7 @@ DenseWs dense_ws_layout(const DenseProblem& p) {
   if (w.max_items < 1) w.max_items = 1;
   w.RP = p.L > 0 ? round_up(p.R > 0 ? p.R : 1, 32) : 0;
   w.npool = p.N1 > 0 ? 2 : 1;
-  w.split = shrink_splits(P, p.H, false);
+  w.split = shrink_splits(P, p.H, false, 1);   // (deeper two-pool splits measured slower here)
   w.ksplit = p.dtype == 1 ? dense_ksplit<bf16_t>(P, p.H, p.N0 + p.N1) : dense_ksplit<float>(P, p.H, p.N0 + p.N1);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up((int64_t)bytes, 256); return o; };
@@ -1789,7 +1792,7 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     s.scaling = p.scaling;
     s.h = h;
     s.cap = w.cap;
-    s.kchunk = shrink_kchunk(P, p.H, false);
+    s.kchunk = shrink_kchunk(P, p.H, false, 1);
     s.split_stride = w.cap * w.npool * w.RP;
     if (w.npool == 2)
       launch_shrink<T, 2>(s, groups, w.split, false, stream);
