@@ -1463,6 +1463,19 @@ static int shrink_splits(int64_t P, int64_t K, bool shared, int npool) {
   return (int)ceil_div(K, shrink_kchunk(P, K, shared, npool));
 }
 
+// A GEMM launch.  With timing events the launch itself takes them (the
+// dispatch records the kernel's start and end: no marker packets between
+// kernels); without, a plain launch, as ordinary callers and stream capture
+// get it.
+template <typename... Args>
+static void launch_timed(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t stream,
+                         hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev0, ev1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+}
+
 ForwardWs forward_ws_layout(const ForwardProblem& p) {
   ForwardWs w;
   const int64_t P = p.T * p.k;
@@ -1609,17 +1622,17 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     if constexpr (kBf16) {
       if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
-        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
+        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       } else if (fp8w) {
         typedef Fp8DecodeCfg F;
-        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
+        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       }
     }
     if (!fp8w)
-      hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
-                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
+      launch_timed((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
+                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
   }
   mark(2 * kStageShrinkA);
   if (lora && groups > 0) {
@@ -1674,17 +1687,17 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     if constexpr (kBf16) {
       if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
-        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
+        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       } else if (fp8w) {
         typedef Fp8DecodeCfg F;
-        hipExtLaunchKernelGGL((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), 0, stream, ev0, ev1, 0, a);
+        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
+                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       }
     }
     if (!fp8w)
-      hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
-                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
+      launch_timed((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
+                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
   }
   mark(2 * kStageCombine);
   if (P > 0) {
@@ -1843,8 +1856,8 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     // the stage's events, when given, are taken by the launch itself
     hipEvent_t ev0 = events ? events[2 * kDenseStageGemm] : nullptr;
     hipEvent_t ev1 = events ? events[2 * kDenseStageGemm + 1] : nullptr;
-    hipExtLaunchKernelGGL((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false, true>),
-                          dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), 0, stream, ev0, ev1, 0, a);
+    launch_timed((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false, true>),
+                          dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
   }
   if (P == 0) mark(2 * kDenseStageGemm + 1);
 
