@@ -44,6 +44,9 @@ def test_route_ties_and_edges():
     _check(lg, 1, "k=1")
     _check(lg[:, :16], 16, "k=E=16")
     _check(rng.standard_normal((300, 1024)).astype(np.float32) * 4, 16, "E=1024 k=16")
+    # more experts than 64 lanes x 16 registers: each scan re-reads the row from memory
+    _check(rng.standard_normal((200, 1500)).astype(np.float32), 8, "E=1500 k=8")
+    _check(rng.integers(-3, 4, size=(64, 1100)).astype(np.float32), 16, "E=1100 ties")
     _check((rng.standard_normal((64, 12)) - 3000).astype(np.float32), 3, "very negative logits")
     _check(np.zeros((0, 8), np.float32), 2, "empty")
 
