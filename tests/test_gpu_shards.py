@@ -7,7 +7,7 @@ the layer (the down expand is linear in the split h).  Expert parallelism gives
 each rank E/G experts; the dispatched (token, expert) pairs arrive as rows
 routed to one local expert, and the returned rows are summed per token.
 
-The tests run every rank of a small layer on this GPU and check that the ranks
+The tests run every rank of a small layer (2, 4 and 8 ranks) on this GPU and check that the ranks
 add up to the oracle's layer, and run the per-rank kernel at the full shard
 shapes (c1 with TP=8, c4 with EP=8) against the oracle on sampled tokens."""
 import numpy as np
@@ -34,11 +34,11 @@ def _tp_shard(inp, G, g, I):
     return out
 
 
-def test_tp_ranks_sum_to_layer():
-    G = 4
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_tp_ranks_sum_to_layer(G):
     spec = workloads.LayerSpec("tp", 8, 2, 256, 512, 3, [16, 8, 0], [45, 30, 21], [0, 1, 2],
                                seed=51, pool_rank=16)
-    say("TP=4 ranks of a small layer")
+    say(f"TP={G} ranks of a small layer")
     inp = gpu_inputs(spec)
     total = None
     for g in range(G):
@@ -51,11 +51,11 @@ def test_tp_ranks_sum_to_layer():
     assert_layer_close(total, oracle_forward(inp), "bf16", "sum of TP ranks")
 
 
-def test_ep_ranks_sum_to_layer():
-    G = 4
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_ep_ranks_sum_to_layer(G):
     spec = workloads.LayerSpec("ep", 8, 2, 256, 256, 3, [16, 8, 16], [40, 27, 33], [0, 1, 2],
                                seed=52, pool_rank=16)
-    say("EP=4 ranks of a small layer")
+    say(f"EP={G} ranks of a small layer")
     inp = gpu_inputs(spec)
     m = inp["meta"]
     T, k = m["topk_ids"].shape
