@@ -430,7 +430,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the layer runs at TP=1 on a single MI355X; there is "
               "no multi-GPU path (the per-rank kernels run at their shard shapes with "
-              "--config c1_tp8, c4p_ep8 or c4d_ep8).", file=sys.stderr)
+              "--config c1_tp2, c1_tp4, c1_tp8, c4p_ep8 or c4d_ep8).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -147,10 +147,11 @@ def config(name: str) -> LayerSpec:
         return LayerSpec(f"{name}_large_expert_{'prefill' if name == 'c4p' else 'decode'}",
                          256, 8, 7168, 2048, 8, [32] * 8, lens, wi, seed=4,
                          router="uniform_bias", pool_rank=32)
-    if name == "c1_tp8":
-        # one rank of c1 under 8-way tensor parallelism: I split 8 ways
+    if name in ("c1_tp2", "c1_tp4", "c1_tp8"):
+        # one rank of c1 under G-way tensor parallelism: I split G ways
+        G = int(name[len("c1_tp"):])
         c1 = config("c1")
-        return LayerSpec("c1_tp8_rank", c1.num_experts, c1.top_k, c1.hidden, c1.inter // 8,
+        return LayerSpec(f"c1_tp{G}_rank", c1.num_experts, c1.top_k, c1.hidden, c1.inter // G,
                          c1.num_loras, c1.lora_ranks, c1.seg_lens, c1.weight_indices,
                          seed=c1.seed, router=c1.router, pool_rank=c1.pool_rank)
     if name in ("c4p_ep8", "c4d_ep8"):
@@ -172,7 +173,7 @@ CONFIG_NAMES = ("c0", "c1", "c2", "c3", "c4p", "c4d")
 # the quantized-weight variants (fp8 e4m3 base weights, bf16 LoRA)
 FP8_CONFIG_NAMES = ("c1_fp8", "c3_fp8", "c4p_fp8", "c4d_fp8")
 # one rank's share of a layer under tensor / expert parallelism (shapes only)
-SHARD_CONFIG_NAMES = ("c1_tp8", "c4p_ep8", "c4d_ep8")
+SHARD_CONFIG_NAMES = ("c1_tp2", "c1_tp4", "c1_tp8", "c4p_ep8", "c4d_ep8")
 
 
 # ----------------------------------------------------------------------------
