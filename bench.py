@@ -165,6 +165,10 @@ class HipEvents:
             out.append(e.value)
         return out
 
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
@@ -205,14 +209,35 @@ def timed_steps(args, torch, hip, step, stages, kernel):
         hip.destroy([e[2 * ki], e[2 * ki + 1]])
     nb = max(1, min(args.steps, 10))
     evb = [hip.create(2 * nst) for _ in range(nb)]
+    evm = [hip.create(3) for _ in range(nb)]   # before info, after info, after align
     for st in range(nb):
-        step(evb[st])
+        step(evb[st], evm[st])
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evb]))
                 for i, name in enumerate(stages)}
-    for e in evb:
+    stage_ms["info"] = float(np.mean([hip.elapsed_ms(e[0], e[1]) for e in evm]))
+    stage_ms["align"] = float(np.mean([hip.elapsed_ms(e[1], e[2]) for e in evm]))
+    for e in evb + evm:
         hip.destroy(e)
     return ms, k_ms, stage_ms
+
+
+def metadata_rates(binding, spec, stage_ms, BM):
+    """info and align: latency-bound, reported in us with the GB/s of their
+    algorithmic bytes as evidence (info: the request arrays, the slot ranks and
+    the two outputs; align: 8 B read and 4 B written per pair plus the tile
+    tables and expert offsets)."""
+    T, k, E, L = spec.num_tokens, spec.top_k, spec.num_experts, spec.num_loras
+    bs, P = spec.num_reqs, spec.num_tokens * spec.top_k
+    cap = binding.moe_lora_align_capacity_rows(T, k, E, L, BM)
+    info_b = 4 * (bs + 1) + 4 * bs + 4 * L + 4 * T + 4 * L
+    align_b = 12 * P + 8 * (cap // BM) + 4 * (E + 1) + 4
+    out = {}
+    for name, nbytes in (("info", info_b), ("align", align_b)):
+        ms = stage_ms[name]
+        out[name] = {"us": round(ms * 1e3, 2), "bytes": int(nbytes),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2) if ms > 0 else None}
+    return out
 
 
 def counts(spec, meta):
@@ -342,11 +367,18 @@ def dense_main(args, torch, binding, workloads, dev):
         device=dev)
     hip = HipEvents()
 
-    def step(events=None):
+    def step(events=None, meta_events=None):
+        stream = torch.cuda.current_stream().cuda_stream
+        if meta_events:
+            hip.record(meta_events[0], stream)
         binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
                               en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+        if meta_events:
+            hip.record(meta_events[1], stream)
         binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, 1, L, BM, out=al,
                                workspace=al_ws)
+        if meta_events:
+            hip.record(meta_events[2], stream)
         binding.moe_lora_dense_forward(inp["x"], inp["w"], N0, al,
                                        inp["lora_ranks"] if L > 0 else None,
                                        inp["scaling"] if L > 0 else None, pools, y=y,
@@ -467,11 +499,18 @@ def main():
 
     hip = HipEvents()
 
-    def step(events=None):
+    def step(events=None, meta_events=None):
+        stream = torch.cuda.current_stream().cuda_stream
+        if meta_events:
+            hip.record(meta_events[0], stream)
         binding.moe_lora_info(T, inp["seg_indptr"], inp["lora_ranks"], inp["weight_indices"],
                               en_buf, mp_buf, max_len=inp["meta"]["max_seg_len"])
+        if meta_events:
+            hip.record(meta_events[1], stream)
         binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, E, L, BM, out=al,
                                workspace=al_ws)
+        if meta_events:
+            hip.record(meta_events[2], stream)
         binding.moe_lora_forward(inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"],
                                  al, k, inp["lora_ranks"] if L > 0 else None,
                                  inp["scaling"] if L > 0 else None, pools, y=y, workspace=fws,
@@ -556,6 +595,7 @@ def main():
                   "algorithmic_flops": c["total_flops"], "algorithmic_bytes": c["total_bytes"],
                   "active_experts": c["active_experts"], "lora_buckets": c["lora_buckets"]},
         "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "metadata": metadata_rates(binding, spec, stage_ms, BM),
         "router_ms": round(router_ms, 4),
     }
     print(json.dumps(out), flush=True)
