@@ -57,10 +57,10 @@ typedef enum { MOE_LORA_F32 = 0, MOE_LORA_BF16 = 1, MOE_LORA_FP8_E4M3 = 2 } moe_
 const char* moe_lora_status_str(int status);
 
 /*
- * moe_lora_route -- the router step before the layer.  The pages' layer
- * configurations define it as softmax over the experts, top-k, renormalised
- * (the workload definitions of the MoE-LoRA pages); the order and the tie rule
- * are this library's reading.
+ * moe_lora_route -- the router step before the layer.  None of the MoE-LoRA
+ * pages describes a router; the layer configurations this library is measured
+ * on define it as softmax over the experts, top-k, renormalised.  The order and
+ * the tie rule are this library's reading.
  *
  *   logits        [num_tokens, num_experts] fp32, row-major, finite values.
  *   topk_ids      [num_tokens, top_k] out  int32: the top_k experts of largest
@@ -180,7 +180,10 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
  *   out_dtype    dtype of y: `dtype` (the default layout) or MOE_LORA_F32 (the fp32
  *                combine result without the final rounding to bf16).
  * num_loras == 0 (pools NULL) runs the plain MoE layer.  H and I must be
- * multiples of 64, R <= 64, top_k <= num_experts.
+ * multiples of 64, R <= 64, top_k <= num_experts.  Size limits (else
+ * MOE_LORA_ERR_UNSUPPORTED): T * H elements of x and 2I * H elements of one
+ * expert's gate_up matrix must each take less than 4 GiB (the GEMMs address
+ * them with 32-bit offsets from 64-bit bases); T * top_k < 2^30.
  * x, the expert weights, the six pools, y and the workspace must be 16-byte
  * aligned (the kernels read and write them in 16-byte units); a misaligned
  * pointer is MOE_LORA_ERR_INVALID.
@@ -289,7 +292,8 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
  *   lora_ranks   [L] int32, scaling [L] float32: as for the MoE layer.
  *   the align outputs, workspace (>= moe_lora_dense_workspace_bytes) and
  *   y            [T, N0 + N1] out  overwritten, in out_dtype (dtype or F32).
- * H, N0 and N1 must be multiples of 64 (N0 > 0, N1 >= 0), R <= 64.  x, w, the
+ * H, N0 and N1 must be multiples of 64 (N0 > 0, N1 >= 0), R <= 64; x and w
+ * must each take less than 4 GiB (else MOE_LORA_ERR_UNSUPPORTED).  x, w, the
  * four pools, y and the workspace must be 16-byte aligned.  Errors and
  * ownership as for moe_lora_forward.
  */

@@ -80,6 +80,13 @@ def lib() -> ctypes.CDLL:
     L.moe_lora_forward_events.restype = ctypes.c_int
     L.moe_lora_forward_events.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.c_void_p,
                                           ctypes.POINTER(ctypes.c_void_p)]
+    L.moe_lora_dense_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_lora_dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseArgs)]
+    L.moe_lora_dense_forward.restype = ctypes.c_int
+    L.moe_lora_dense_forward.argtypes = [ctypes.POINTER(DenseArgs), ctypes.c_void_p]
+    L.moe_lora_dense_forward_events.restype = ctypes.c_int
+    L.moe_lora_dense_forward_events.argtypes = [ctypes.POINTER(DenseArgs), ctypes.c_void_p,
+                                                ctypes.POINTER(ctypes.c_void_p)]
     _LIB = L
     return L
 

@@ -13,6 +13,9 @@ namespace {
 
 constexpr int64_t kMaxKeys = 32768;  // E * (L + 1) supported by the align kernels
 constexpr int64_t kMaxRank = 64;
+// x [T, H] and one expert's (or the dense projection's) weight matrix must each
+// stay below 4 GiB: the GEMMs address them with 32-bit byte offsets
+constexpr int64_t kMaxOffsetBytes = int64_t(1) << 32;
 
 bool bad_block_m(int32_t bm) { return bm < 16 || bm > 256 || (bm % 16) != 0; }
 
@@ -116,6 +119,15 @@ static int to_problem(const moe_lora_forward_args* a, ForwardProblem* p, bool ch
   if (a->max_rank > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
   if ((int64_t)a->num_tokens * a->top_k > INT32_MAX / 2) return MOE_LORA_ERR_UNSUPPORTED;
   if (a->num_loras > 0 && a->max_rank <= 0) return MOE_LORA_ERR_INVALID;
+  {
+    // the GEMMs address gathered x rows and one expert's weight matrix with
+    // 32-bit byte offsets from 64-bit bases
+    const int64_t esz = a->dtype == MOE_LORA_BF16 ? 2 : 4;
+    const int64_t wsz = (has_w && a->weight_dtype == MOE_LORA_FP8_E4M3) ? 1 : esz;
+    if ((int64_t)a->num_tokens * a->hidden * esz >= kMaxOffsetBytes ||
+        2 * (int64_t)a->inter * a->hidden * wsz >= kMaxOffsetBytes)
+      return MOE_LORA_ERR_UNSUPPORTED;
+  }
   if (check_ptrs && a->num_tokens > 0) {
     if (!a->x || !a->topk_weights || !a->w_gate_up || !a->w_down || !a->sorted_pair_ids ||
         !a->tile_expert || !a->tile_lora || !a->expert_tile_offsets || !a->num_rows_padded || !a->y)
@@ -197,6 +209,12 @@ static int to_dense(const moe_lora_dense_args* a, DenseProblem* p, bool check_pt
   if (a->max_rank > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
   if (a->num_loras > 0 && a->max_rank <= 0) return MOE_LORA_ERR_INVALID;
   if ((int64_t)a->num_loras + 1 > kMaxKeys) return MOE_LORA_ERR_UNSUPPORTED;
+  {
+    const int64_t esz = a->dtype == MOE_LORA_BF16 ? 2 : 4;
+    if ((int64_t)a->num_tokens * a->hidden * esz >= kMaxOffsetBytes ||
+        ((int64_t)a->out0 + a->out1) * a->hidden * esz >= kMaxOffsetBytes)
+      return MOE_LORA_ERR_UNSUPPORTED;
+  }
   if (a->out_dtype != a->dtype && a->out_dtype != MOE_LORA_F32) return MOE_LORA_ERR_UNSUPPORTED;
   if (check_ptrs && a->num_tokens > 0) {
     if (!a->x || !a->w || !a->sorted_pair_ids || !a->tile_expert || !a->tile_lora ||

@@ -727,7 +727,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   auto swzb = [](int n) -> int {
     return ROWB_B == 128 ? ((n >> 1) & 7) : ((n >> 2) & 3);
   };
-  const T* a_base = a.a_src;
+  // 64-bit bases; the per-lane DMA offsets below are 32-bit.  A non-gathered
+  // A operand (act) starts at the tile's first row, so its offsets stay below
+  // BM * K elements whatever the batch; gathered x rows and one expert's
+  // weights are kept under 4 GiB by the host checks.
+  const T* a_base = GATHER ? a.a_src : a.a_src + row0 * a.K;
   const W* b_base = static_cast<const W*>(a.w) + (int64_t)e * a.w_rows * a.K;
   // global row (of a_base for row < BM, of b_base otherwise) behind LDS row `row`
   auto grow_of = [&](int row, int pid_in) -> int64_t {
@@ -737,7 +741,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
         const int pid = r < nrows ? pid_in : a.P;
         return pid < a.P ? pid / a.top_k : 0;
       }
-      return row0 + (r < nrows ? r : 0);
+      return r < nrows ? r : 0;   // relative to the tile's first row
     }
     const int n = row - BM;
     if (GATE_UP) {

@@ -1,8 +1,9 @@
 // Router step before the layer: per token, the top_k experts of largest
 // softmax probability (descending, ties to the lower expert id) and their
-// probabilities renormalised over the k.  The layer configs of the pages'
-// workloads define the router as softmax, top-k, renormalised; the tie rule
-// and the descending order are this library's reading.
+// probabilities renormalised over the k.  None of the MoE-LoRA pages describes
+// a router: the layer configurations this library is measured on define it as
+// softmax over the experts, top-k, renormalised; the tie rule and the
+// descending order are this library's reading.
 //
 // Softmax is strictly increasing in the logit, so the ranking is taken on the
 // logits themselves (exact fp32 input values), and in the renormalised weight

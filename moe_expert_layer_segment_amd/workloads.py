@@ -20,8 +20,11 @@ silent:
 * Router: float64 softmax over experts, top-k by descending probability with
   ties going to the lower expert id, weights renormalised over the top-k and
   stored as float32.
-* Each tensor (and each expert slice of it) has its own sub-seed derived from
-  ``(seed, tensor_id, expert)``, so any expert can be regenerated on its own.
+* Each expert weight has its own sub-seed derived from ``(seed, tensor_id,
+  expert)``, and each LoRA pool slot (all experts at once) from ``(seed,
+  tensor_id, slot)``, so any expert or slot can be regenerated on its own.  A
+  pool is drawn with one call per slot, which keeps the number of device
+  launches of a large configuration in the hundreds.
 * fp8 expert weights: each expert's fp32 draw is quantized to OCP e4m3 codes
   over 128 x 128 blocks; x, pools and y stay bf16.  ``weights="fp8"`` uses
   power-of-two block scales, 2^ceil(log2(amax / 448)) (448 = the largest finite
@@ -300,8 +303,9 @@ def generate(spec: LayerSpec, device="cpu", canary: bool = True,
                 r = int(ranks[l])
                 if r == 0:
                     continue
-                for e in range(E):
-                    pool[l, e, :r] = _randn((r, dim), std, _subseed(s, tid, l * 65536 + e), dev, dt)
+                # one draw per (pool, slot) covering every expert: a handful of
+                # device launches per pool instead of one set per (slot, expert)
+                pool[l, :, :r] = _randn((E, r, dim), std, _subseed(s, tid, l), dev, dt)
             pools[name] = pool
         out.update(pools)
     out["topk_ids"] = torch.from_numpy(ids).to(dev)

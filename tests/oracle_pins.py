@@ -190,6 +190,59 @@ def pin_align_lexsort(orc):
         assert row <= got.shape[0] == orc.align_capacity_rows(P, E, L, BM)
 
 
+def _capacity_case(E, L, k, keys_per_pair, BM=16):
+    """Align inputs whose pair p lands in bucket keys_per_pair[p] = (expert, slot)
+    (top-k rows built so that a token's experts are distinct, every slot enabled)."""
+    P = len(keys_per_pair)
+    T = P // k
+    ids = np.zeros((T, k), np.int32)
+    mapping = np.zeros(T, np.int32)
+    for t in range(T):
+        slots = {keys_per_pair[t * k + j][1] for j in range(k)}
+        assert len(slots) == 1, "one slot per token"
+        mapping[t] = slots.pop()
+        for j in range(k):
+            ids[t, j] = keys_per_pair[t * k + j][0]
+        assert len(set(ids[t].tolist())) == k
+    enabled = np.ones(L, np.int32)
+    return ids, mapping, enabled
+
+
+def pin_align_capacity_tight(orc):
+    """The capacity P + min(P, E(L+1)) * (BM - 1), rounded up to BM, is reached:
+    (a) when every pair has a bucket of its own (P <= E(L+1)): P * BM rows;
+    (b) when every key is used and every bucket holds 1 pair modulo BM
+        (P > E(L+1)): P + E(L+1) * (BM - 1) rows.  The written-out values below
+    follow from the worst-case construction, not from the formula."""
+    BM = 16
+    # (a) E = 8, L = 3 (32 keys), 16 pairs, k = 2: tokens alternate expert pairs
+    # over the 4 slot values, so all 16 keys differ -> 16 buckets x 16 rows = 256
+    keys = []
+    for t in range(8):
+        a = t // 2 - 1
+        e0 = 2 * (t % 2) + 4 * (t // 4)
+        keys += [(e0, a), (e0 + 1, a)]
+    ids, mapping, enabled = _capacity_case(8, 3, 2, keys)
+    out = orc.moe_lora_align(ids, mapping, enabled, 8, 3, BM)
+    assert int(out["num_rows_padded"][0]) == 256
+    assert orc.align_capacity_rows(16, 8, 3, BM) == 256 == out["sorted_pair_ids"].shape[0]
+    # (b) E = 4, L = 3 (16 keys), k = 1: key 0 holds 17 pairs, the other 15 one
+    # each -> P = 32 pairs in 16 buckets of 1 (mod 16): 2 + 15 = 17 tiles = 272 rows
+    keys = [(0, -1)] * 17 + [(e, a) for e in range(4) for a in range(-1, 3)][1:]
+    ids, mapping, enabled = _capacity_case(4, 3, 1, keys)
+    out = orc.moe_lora_align(ids, mapping, enabled, 4, 3, BM)
+    assert int(out["num_rows_padded"][0]) == 272
+    assert orc.align_capacity_rows(32, 4, 3, BM) == 272 == out["sorted_pair_ids"].shape[0]
+    # the workloads' shapes, evaluated by hand: P + min(P, E(L+1)) * 15, rounded up to 16
+    for (P, E, L, want) in [(54, 8, 4, 656),        # 54 + 40 * 15 = 654
+                            (8192, 8, 8, 9280),     # 8192 + 72 * 15 = 9272
+                            (65536, 128, 16, 98176),  # 65536 + 2176 * 15
+                            (512, 128, 32, 8192),   # 512 + 512 * 15
+                            (131072, 256, 8, 165632),  # 131072 + 2304 * 15
+                            (1024, 256, 8, 16384)]:  # 1024 + 1024 * 15
+        assert orc.align_capacity_rows(P, E, L, BM) == want, (P, E, L)
+
+
 def pin_align_bruteforce(orc):
     rng = np.random.default_rng(5)
     for _ in range(30):
@@ -511,6 +564,20 @@ def pin_block_dequant(orc):
     mask = np.zeros_like(d)
     mask[1, 0:128, 256:384] = vals[1, 0:128, 256:384] != 0
     assert np.array_equal(d, mask)
+
+
+def pin_block_dequant_golden(orc):
+    """Hand-computed E4M3 block dequantization (tests/golden/fp8_block_dequant.json)."""
+    g = _load("fp8_block_dequant.json")
+    n, k = g["shape"]
+    codes = np.zeros((n, k), np.uint8)
+    for ent in g["entries"]:
+        codes[ent["n"], ent["k"]] = int(ent["code"], 16)
+    w = orc.dequantize_block_fp8(codes, np.asarray(g["scales"], np.float64), g["block"])
+    want = np.zeros((n, k))
+    for ent in g["entries"]:
+        want[ent["n"], ent["k"]] = ent["expected"]
+    assert np.array_equal(w, want), np.argwhere(w != want)[:5]
 
 
 # ---------------------------------------------------------------------------

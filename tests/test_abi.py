@@ -240,3 +240,38 @@ def test_binding_refuses_host_tensors():
         binding.moe_lora_info(3, torch.tensor([0, 3], dtype=torch.int32),
                               torch.tensor([4], dtype=torch.int32),
                               torch.tensor([0], dtype=torch.int32))
+
+
+def test_size_limits_of_32bit_offsets():
+    """x [T, H] and one expert's weight matrix are addressed with 32-bit byte
+    offsets from 64-bit bases: sizes reaching 4 GiB are refused before launch."""
+    lib = binding.lib()
+    call = lambda **o: lib.moe_lora_forward(ctypes.byref(_fargs(**o)), None)  # noqa: E731
+    ws = lambda **o: lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(**o)))  # noqa: E731
+    # bf16 x of 2^20 tokens x 2048 = 4 GiB: refused; one token fewer is accepted
+    assert call(num_tokens=1 << 20, top_k=1, hidden=2048) == binding.ERR_UNSUPPORTED
+    assert ws(num_tokens=1 << 20, top_k=1, hidden=2048) == 0
+    assert call(num_tokens=(1 << 20) - 1, top_k=1, hidden=2048) == binding.ERR_WORKSPACE
+    # fp32 halves the token limit
+    f32 = dict(dtype=binding.DTYPE_F32, out_dtype=binding.DTYPE_F32)
+    assert call(num_tokens=1 << 19, top_k=1, hidden=2048, **f32) == binding.ERR_UNSUPPORTED
+    # one expert's gate_up matrix: 2 * I * H * 2 bytes < 4 GiB
+    assert call(hidden=32768, inter=32768) == binding.ERR_UNSUPPORTED
+    assert call(hidden=16384, inter=32768) == binding.ERR_WORKSPACE
+    # the dense projection: x and w likewise
+    dcall = lambda **o: lib.moe_lora_dense_forward(ctypes.byref(_dargs(**o)), None)  # noqa: E731
+    assert dcall(num_tokens=1 << 20, hidden=2048) == binding.ERR_UNSUPPORTED
+    assert dcall(hidden=65536, out0=32768, out1=0, a1=None, b1=None) == binding.ERR_UNSUPPORTED
+
+
+def test_dense_ctypes_signatures_return_size_t():
+    """The dense sizing call returns a size_t: without a declared restype ctypes
+    would truncate it to a C int above 2 GiB."""
+    lib = binding.lib()
+    assert lib.moe_lora_dense_workspace_bytes.restype is ctypes.c_size_t
+    assert lib.moe_lora_forward_workspace_bytes.restype is ctypes.c_size_t
+    # a large dense batch (8M tokens x 2048 bf16 outputs: the fp32 partials alone are 64 GiB)
+    big = lib.moe_lora_dense_workspace_bytes(ctypes.byref(_dargs(num_tokens=1 << 23, hidden=128,
+                                                                 out0=2048, out1=0, a1=None,
+                                                                 b1=None)))
+    assert big > (1 << 34)

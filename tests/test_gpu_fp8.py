@@ -67,17 +67,24 @@ def test_fp8_down_k_split(E, lens):
     assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", "fp8 down K split")
 
 
-@pytest.mark.parametrize("name,n_sample", [("c1_fp8", 40), ("c3_fp8", 40), ("c4d_fp8", 16),
-                                           ("c4p_fp8", 12)])
-def test_fp8_full_size_sampled(name, n_sample):
+@pytest.mark.parametrize("name,n_sample", [("c1_fp8", 40), ("c4p_fp8", 12), ("c3_fp8", 0),
+                                           ("c4d_fp8", 0)])
+def test_fp8_full_size(name, n_sample):
+    """Prefill batches on a strided token sample; the decode batches (64 and 128
+    tokens) on every token (n_sample 0)."""
     spec = workloads.config(name)
     say(f"forward full-size {name}: T={spec.num_tokens}")
     inp = gpu_inputs(spec)
     got = to_np(run(inp, out_dtype=torch.float32))
     assert np.all(np.isfinite(got))
     T = spec.num_tokens
-    sample = np.unique(np.concatenate([np.linspace(0, T - 1, n_sample).astype(np.int64), [0, T - 1]]))
-    ref = oracle_forward(inp, tokens=sample)
-    assert_layer_close(got[sample], ref, "bf16", f"{name} ({len(sample)} sampled tokens)")
+    if n_sample:
+        sample = np.unique(np.concatenate([np.linspace(0, T - 1, n_sample).astype(np.int64),
+                                           [0, T - 1]]))
+        ref = oracle_forward(inp, tokens=sample)
+        assert_layer_close(got[sample], ref, "bf16", f"{name} ({len(sample)} sampled tokens)")
+    else:
+        ref = oracle_forward(inp)
+        assert_layer_close(got, ref, "bf16", f"{name} (all {T} tokens)")
     del inp
     torch.cuda.empty_cache()

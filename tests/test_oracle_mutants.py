@@ -46,6 +46,11 @@ MUTANTS = {
                          "y[m, :N0] += ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])"),
     "dense_full_pool_rows": ("y[m, :N0] += s * ((X[m] @ _f64(a0[l])[:r].T) @ _f64(b0[l])[:r])",
                              "y[m, :N0] += s * ((X[m] @ _f64(a0[l]).T) @ _f64(b0[l]))"),
+    "capacity_no_min": ("nb = min(num_pairs, num_experts * (num_loras + 1))",
+                        "nb = num_experts * (num_loras + 1)"),
+    "capacity_pads_full_block": ("rows = num_pairs + nb * (block_m - 1)", "rows = num_pairs + nb * block_m"),
+    "dequant_block_transposed": ("s_full = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)",
+                                 "s_full = np.repeat(np.repeat(np.swapaxes(s, -1, -2), block, axis=-2), block, axis=-1)"),
     "brute_b_untransposed": ("Bd = _f64(b_down[l, e])[:r].T      # [H, r]", "Bd = _f64(b_down[l, e])[:r].T[::-1]"),
 }
 
