@@ -2,14 +2,16 @@
 """Throughput of the MoE expert layer with per-request LoRA deltas on one MI355X.
 
 A step is one pass of the whole hot path over one batch: moe_lora_info (the
-per-batch metadata), moe_lora_align and moe_lora_forward, on the Mixtral-shaped
-prefill workload (8 experts, top-2, hidden 4096, intermediate 14336, 4096
-tokens in 16 requests, 8 adapter slots of rank 16, bf16) unless --config says
-otherwise.  Inputs are synthetic and resident in HBM before timing starts.
+per-batch metadata), moe_lora_align and moe_lora_forward.  The default workload
+is the largest layer that fits one GPU: 256 routed experts, top-8, hidden 7168,
+moe intermediate 2048 (22.5 GB of expert weights), 8 adapter slots of rank 32,
+one prefill batch of 16384 tokens in 64 requests, bf16 (--config picks another).
+Inputs are synthetic and resident in HBM before timing starts.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel (the
-gate_up GEMM, timed with HIP events around its launch inside the timed region)
-and the CPU oracle timed on a bounded sample of the same workload.
+gate_up GEMM, timed with HIP events around its launch inside the timed region),
+the median of graph replays of [align -> forward], and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,10 +37,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c1")
+    ap.add_argument("--config", default="c4p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="tokens of the batch the CPU oracle runs on (0: all of them)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=-1,
+                    help="tokens of the batch the CPU oracle runs on (0: all of them; -1: as "
+                         "many as about 1.5 TFLOP of oracle work)")
+    ap.add_argument("--graph-replays", type=int, default=50,
+                    help="HIP-graph replays of [align -> forward] timed one by one (median)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle pass over the sample until this much time has passed")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -220,6 +225,48 @@ def timed_steps(args, torch, hip, step, stages, kernel):
     for e in evb + evm:
         hip.destroy(e)
     return ms, k_ms, stage_ms
+
+
+def graph_replays(torch, hip, fn, n):
+    """Capture fn ([align -> forward]) in a HIP graph and time n replays one by
+    one, each between two fence-free events on the replay stream; returns
+    (median ms, min ms, max ms).  The library launches kernels only (no
+    allocation, memset or host synchronisation), so the capture holds the same
+    kernels the eager step runs."""
+    if n <= 0:
+        return None
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [hip.create(2) for _ in range(n)]
+    for a, b in evs:
+        hip.record(a, stream)
+        g.replay()
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = np.array([hip.elapsed_ms(a, b) for a, b in evs])
+    for e in evs:
+        hip.destroy(e)
+    del g
+    return float(np.median(ms)), float(ms.min()), float(ms.max())
+
+
+def default_cpu_sample(spec):
+    """Tokens of the batch for the CPU oracle: about 1.5 TFLOP of float64 work
+    (10-30 s on the host's cores with the oracle's per-expert BLAS products)."""
+    per_token = 6.0 * spec.hidden * spec.inter * spec.top_k
+    return int(min(spec.num_tokens, max(64, 1.5e12 // per_token)))
 
 
 def metadata_rates(binding, spec, stage_ms, BM):
@@ -527,6 +574,24 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
+    def align_forward():
+        binding.moe_lora_align(inp["topk_ids"], mp, en if L > 0 else None, E, L, BM, out=al,
+                               workspace=al_ws)
+        binding.moe_lora_forward(inp["x"], inp["topk_weights"], inp["w_gate_up"], inp["w_down"],
+                                 al, k, inp["lora_ranks"] if L > 0 else None,
+                                 inp["scaling"] if L > 0 else None, pools, y=y, workspace=fws,
+                                 w_scales=w_scales)
+
+    graph = None
+    if args.graph_replays > 0:
+        gmed, gmin, gmax = graph_replays(torch, hip, align_forward, args.graph_replays)
+        graph = {"what": "align + forward captured in one HIP graph; info once per batch",
+                 "replays": args.graph_replays, "median_ms": round(gmed, 4),
+                 "min_ms": round(gmin, 4), "max_ms": round(gmax, 4),
+                 "tokens_per_s": round(T / (gmed * 1e-3), 1)}
+        print(f"[bench] {args.graph_replays} graph replays: median {gmed:.3f} ms", file=sys.stderr,
+              flush=True)
+
     # the router step before the layer (not part of the step): its time on this
     # workload's router logits, events on the current stream (the launch stream)
     logits = torch.from_numpy(workloads.router_logits(spec).astype(np.float32)).to(dev)
@@ -567,8 +632,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(spec, inp, args.cpu_sample_tokens, args.cpu_min_seconds)
+        n_cpu = default_cpu_sample(spec) if args.cpu_sample_tokens < 0 else args.cpu_sample_tokens
+        print(f"[bench] timing the CPU oracle on a sample of {n_cpu or T} tokens", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(spec, inp, n_cpu, args.cpu_min_seconds)
 
     tok_s = T / (ms * 1e-3)
     out = {
@@ -594,6 +661,7 @@ def main():
                   "gbs": round(c["total_bytes"] / (ms * 1e-3) / 1e9, 1),
                   "algorithmic_flops": c["total_flops"], "algorithmic_bytes": c["total_bytes"],
                   "active_experts": c["active_experts"], "lora_buckets": c["lora_buckets"]},
+        "graph": graph,
         "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
         "metadata": metadata_rates(binding, spec, stage_ms, BM),
         "router_ms": round(router_ms, 4),

@@ -155,6 +155,38 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Device-side precondition checks (MOE_LORA_DEBUG builds, libmoe_lora_debug.so).
+ *
+ * Release builds never read device data on the host and treat device-side
+ * precondition violations as undefined input (they never cause out-of-bounds
+ * accesses: align drops pairs whose expert id is out of range, info ignores
+ * out-of-range slots for adapter_enabled).  A library built with
+ * MOE_LORA_DEBUG defined additionally checks, inside its kernels:
+ *   MOE_LORA_DEBUG_SEG_INDPTR    (info)  seg_indptr[0] == 0, nondecreasing,
+ *                                        seg_indptr[num_reqs] == num_tokens
+ *   MOE_LORA_DEBUG_WEIGHT_INDEX  (info)  -1 <= weight_indices[b] < num_loras
+ *   MOE_LORA_DEBUG_RANK          (info)  lora_ranks[i] >= 0
+ *   MOE_LORA_DEBUG_EXPERT_ID     (align) 0 <= topk_ids[p] < num_experts
+ *   MOE_LORA_DEBUG_MAPPING       (align) -1 <= token_lora_mapping[t] < num_loras
+ * and ORs the bit of each violated check into a device word of the library
+ * (one per device, shared by every call on it; the page on sharing the MoE
+ * LoRA batch info, section 评论区精华, is about such a -1 index reaching a
+ * scatter).  The results of the calls are those of the release build.
+ *
+ * moe_lora_debug_flags synchronises `stream`, writes the word to *flags and,
+ * when `clear` is nonzero, resets it to 0.  A release build writes 0 and
+ * returns MOE_LORA_ERR_UNSUPPORTED.  flags NULL is MOE_LORA_ERR_INVALID.
+ */
+enum {
+  MOE_LORA_DEBUG_SEG_INDPTR = 1,
+  MOE_LORA_DEBUG_WEIGHT_INDEX = 2,
+  MOE_LORA_DEBUG_RANK = 4,
+  MOE_LORA_DEBUG_EXPERT_ID = 8,
+  MOE_LORA_DEBUG_MAPPING = 16
+};
+int moe_lora_debug_flags(uint32_t* flags, int32_t clear, void* stream);
+
+/*
  * Arguments of moe_lora_forward.  All tensors are row-major and contiguous.
  * `dtype` applies to x, the expert weights, the six pools and y.
  *

@@ -15,6 +15,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LORA_LIB") or os.path.join(_PKG, "lib", "libmoe_lora.so")
+# the same library built with MOE_LORA_DEBUG (device-side precondition checks)
+DEBUG_LIB_PATH = os.path.join(_PKG, "lib", "libmoe_lora_debug.so")
 
 OK, ERR_INVALID, ERR_UNDERCOVER, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
@@ -48,18 +50,33 @@ class ForwardArgs(ctypes.Structure):
 
 
 _LIB = None
+_DEBUG_LIB = None
 
 
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    if not os.path.exists(LIB_PATH):
+    if _LIB is None:
+        _LIB = _load(LIB_PATH)
+    return _LIB
+
+
+def debug_lib() -> ctypes.CDLL:
+    """The MOE_LORA_DEBUG build of the library (same calls, same results; info
+    and align also flag device-side precondition violations, read with
+    ``moe_lora_debug_flags``)."""
+    global _DEBUG_LIB
+    if _DEBUG_LIB is None:
+        _DEBUG_LIB = _load(DEBUG_LIB_PATH)
+    return _DEBUG_LIB
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"MoE-LoRA HIP library not found at {LIB_PATH}; build it with "
+            f"MoE-LoRA HIP library not found at {path}; build it with "
             "`python -m moe_expert_layer_segment_amd.build` (no CPU fallback exists)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     L.moe_lora_status_str.restype = ctypes.c_char_p
     L.moe_lora_status_str.argtypes = [ctypes.c_int]
     L.moe_lora_route.restype = ctypes.c_int
@@ -87,8 +104,22 @@ def lib() -> ctypes.CDLL:
     L.moe_lora_dense_forward_events.restype = ctypes.c_int
     L.moe_lora_dense_forward_events.argtypes = [ctypes.POINTER(DenseArgs), ctypes.c_void_p,
                                                 ctypes.POINTER(ctypes.c_void_p)]
-    _LIB = L
+    L.moe_lora_debug_flags.restype = ctypes.c_int
+    L.moe_lora_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                       ctypes.c_void_p]
     return L
+
+
+DEBUG_SEG_INDPTR, DEBUG_WEIGHT_INDEX, DEBUG_RANK, DEBUG_EXPERT_ID, DEBUG_MAPPING = 1, 2, 4, 8, 16
+
+
+def debug_flags(clear: bool = True, library: Optional[ctypes.CDLL] = None) -> int:
+    """The precondition flag word of a MOE_LORA_DEBUG build (after synchronising
+    the current stream); ``clear`` resets it."""
+    L = library or debug_lib()
+    v = ctypes.c_uint32(0)
+    _check(L.moe_lora_debug_flags(ctypes.byref(v), int(clear), _stream()), "moe_lora_debug_flags")
+    return int(v.value)
 
 
 class MoeLoraError(RuntimeError):

@@ -2,8 +2,11 @@
 
     python -m moe_expert_layer_segment_amd.build
 
-Produces ``moe_expert_layer_segment_amd/lib/libmoe_lora.so``.  Every HIP source
-is compiled for gfx950 only, with packed-fp32 instruction selection disabled.
+Produces ``moe_expert_layer_segment_amd/lib/libmoe_lora.so`` and its
+``MOE_LORA_DEBUG`` twin ``lib/libmoe_lora_debug.so`` (the same kernels; info and
+align additionally check their device-side preconditions and flag violations
+in a device word).  Every HIP source is compiled for gfx950 only, with
+packed-fp32 instruction selection disabled.
 """
 from __future__ import annotations
 
@@ -19,9 +22,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_lora.so")
+DEBUG_LIB = os.path.join(LIBDIR, "libmoe_lora_debug.so")
 BUILD = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "route.hip", "info.hip", "align.hip", "forward.hip"]
+# sources whose code differs under MOE_LORA_DEBUG (the rest is shared)
+DEBUG_SOURCES = ["api.cpp", "info.hip", "align.hip"]
 ARCH = "gfx950"
 
 
@@ -38,9 +44,10 @@ def common_flags():
             "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, debug: bool = False) -> str:
+    out = os.path.join(BUILD, ("debug_" if debug else "") + os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + common_flags() + (["-DMOE_LORA_DEBUG"] if debug else []) + \
+        ["-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,19 +56,27 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in DEBUG_SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    release = objs[:len(SOURCES)]
+    debug = dict(zip(DEBUG_SOURCES, objs[len(SOURCES):]))
+    _link(release, LIB)
+    _link([debug.get(s, o) for s, o in zip(SOURCES, release)], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

@@ -13,6 +13,7 @@
 //                 bucket offset + chunk prefix + rank; pads, tile tables and the
 //                 unused tail are filled by binary search over bucket starts.
 // Every output word up to the capacity is written.
+#include "moe_lora.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__(256)
 align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves, int steps,
                    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ mapping,
                    const int32_t* __restrict__ enabled, int32_t* __restrict__ ws_rank,
-                   int32_t* __restrict__ ws_cnt) {
+                   int32_t* __restrict__ ws_cnt, uint32_t* __restrict__ dbg) {
   extern __shared__ uint16_t hist[];  // [waves][K]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint16_t* h = hist + (size_t)wave * K;
@@ -85,7 +86,16 @@ align_count_kernel(int P, int k, int E, int L, int K, int key_bits, int waves, i
   for (int s = 0; s < kAlignSteps; ++s) {
     const int64_t p = wbase + s * 64 + lane;
     int key = -1;
-    if (s < steps && p < P) key = pair_key((int)p, k, E, L, topk_ids, mapping, enabled);
+    if (s < steps && p < P) {
+      key = pair_key((int)p, k, E, L, topk_ids, mapping, enabled);
+#ifdef MOE_LORA_DEBUG
+      // preconditions: expert ids in [0, E), the token's slot in [-1, L)
+      const int32_t e = topk_ids[p];
+      if (e < 0 || e >= E) debug_flag(dbg, MOE_LORA_DEBUG_EXPERT_ID);
+      const int32_t a = mapping[p / k];
+      if (p % k == 0 && (a < -1 || a >= L)) debug_flag(dbg, MOE_LORA_DEBUG_MAPPING);
+#endif
+    }
     const bool valid = key >= 0;
     // lanes holding the same key: AND of per-bit ballots
     uint64_t m = __ballot(valid);
@@ -268,7 +278,7 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
                         const int32_t* topk_ids, const int32_t* mapping, const int32_t* enabled,
                         int32_t* sorted_ids, int32_t* tile_expert, int32_t* tile_lora,
                         int32_t* expert_tile_offsets, int32_t* num_rows_padded, void* workspace,
-                        hipStream_t stream) {
+                        uint32_t* debug_word, hipStream_t stream) {
   const int64_t P = (int64_t)T * k;
   const int64_t K = (int64_t)E * (L + 1);
   const AlignWs w = align_ws_layout(P, K);
@@ -284,7 +294,7 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
 
   hipLaunchKernelGGL(align_count_kernel, dim3((unsigned)w.nchunks), dim3(64 * waves), lds, stream,
                      (int)P, k, E, L, (int)K, key_bits, waves, align_steps(P, K), topk_ids, mapping,
-                     enabled, ws_rank, ws_cnt);
+                     enabled, ws_rank, ws_cnt, debug_word);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, (int)w.nchunks,
                      (int)K, E, L, BM, ws_cnt, ws_bstart, ws_btotal, expert_tile_offsets,
                      num_rows_padded);

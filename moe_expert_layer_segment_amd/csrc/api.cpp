@@ -60,7 +60,7 @@ int moe_lora_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras, int32
   if (num_tokens > 0 && !token_lora_mapping) return MOE_LORA_ERR_INVALID;
   if (num_tokens == 0 && num_loras == 0) return MOE_LORA_OK;
   return hip_status(launch_info(num_tokens, num_reqs, num_loras, seg_indptr, weight_indices,
-                                lora_ranks, adapter_enabled, token_lora_mapping,
+                                lora_ranks, adapter_enabled, token_lora_mapping, debug_word(),
                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -97,7 +97,14 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
   return hip_status(launch_align(num_tokens, top_k, num_experts, num_loras, block_m, topk_ids,
                                  token_lora_mapping, adapter_enabled, sorted_pair_ids, tile_expert,
                                  tile_lora, expert_tile_offsets, num_rows_padded, workspace,
-                                 static_cast<hipStream_t>(stream)));
+                                 debug_word(), static_cast<hipStream_t>(stream)));
+}
+
+int moe_lora_debug_flags(uint32_t* flags, int32_t clear, void* stream) {
+  if (!flags) return MOE_LORA_ERR_INVALID;
+  *flags = 0;
+  if (!debug_word()) return MOE_LORA_ERR_UNSUPPORTED;   // a release build: no checks
+  return hip_status(debug_word_read(flags, clear != 0, static_cast<hipStream_t>(stream)));
 }
 
 // the kernels move activations, weights, pools and outputs in 16-byte units
@@ -198,6 +205,7 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
   if (!events) return MOE_LORA_ERR_INVALID;
   return forward_impl(args, stream, events);
 }
+
 
 static int to_dense(const moe_lora_dense_args* a, DenseProblem* p, bool check_ptrs) {
   if (!a || a->struct_size < sizeof(moe_lora_dense_args)) return MOE_LORA_ERR_INVALID;

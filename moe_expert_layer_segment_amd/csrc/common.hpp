@@ -77,6 +77,19 @@ __device__ inline float silu_f(float v) {
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// Device-side precondition checks of MOE_LORA_DEBUG builds: a violated
+// precondition sets its bit in one device word (a vector atomic OR; the word's
+// address is passed to the kernels, null in release builds, where the checks
+// are compiled out).  The bits are those of MOE_LORA_DEBUG_* in moe_lora.h.
+__device__ inline void debug_flag(uint32_t* word, uint32_t bit) {
+#ifdef MOE_LORA_DEBUG
+  if (word) atomicOr(word, bit);
+#else
+  (void)word;
+  (void)bit;
+#endif
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.  Used
 // where an index selects accumulator registers, so the body is always
 // instantiated per index (never left as a runtime loop over a register array).

@@ -1891,4 +1891,5 @@ hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t 
   return run_forward<float>(p, workspace, stream, events);
 }
 
+
 }  // namespace moelora

@@ -7,6 +7,7 @@
 // One launch, token-parallel: each thread binary-searches seg_indptr for the
 // request that owns its token, so coverage never depends on a max-length hint.
 // Workgroup 0 additionally builds adapter_enabled through an LDS flag array.
+#include "moe_lora.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,8 +20,24 @@ __global__ void __launch_bounds__(kInfoThreads)
 info_kernel(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
             const int32_t* __restrict__ seg_indptr, const int32_t* __restrict__ weight_indices,
             const int32_t* __restrict__ lora_ranks, int32_t* __restrict__ adapter_enabled,
-            int32_t* __restrict__ token_lora_mapping) {
+            int32_t* __restrict__ token_lora_mapping, uint32_t* __restrict__ dbg) {
   const int t = blockIdx.x * kInfoThreads + threadIdx.x;
+#ifdef MOE_LORA_DEBUG
+  // preconditions: seg_indptr starts at 0, is nondecreasing and ends at
+  // num_tokens; weight_indices in [-1, num_loras); lora_ranks >= 0
+  for (int64_t i = t; i <= (int64_t)max(num_reqs, num_loras); i += (int64_t)gridDim.x * kInfoThreads) {
+    if (i < num_reqs) {
+      const int32_t a = seg_indptr[i], b = seg_indptr[i + 1];
+      if (b < a || (i == 0 && a != 0) || (i == num_reqs - 1 && b != num_tokens))
+        debug_flag(dbg, MOE_LORA_DEBUG_SEG_INDPTR);
+      const int32_t wi = weight_indices[i];
+      if (wi < -1 || wi >= num_loras) debug_flag(dbg, MOE_LORA_DEBUG_WEIGHT_INDEX);
+    }
+    if (i == 0 && num_reqs == 0 && (seg_indptr[0] != 0 || num_tokens != 0))
+      debug_flag(dbg, MOE_LORA_DEBUG_SEG_INDPTR);
+    if (i < num_loras && lora_ranks[i] < 0) debug_flag(dbg, MOE_LORA_DEBUG_RANK);
+  }
+#endif
   if (t < num_tokens) {
     // last b with seg_indptr[b] <= t (empty segments are skipped naturally)
     int lo = 0, hi = num_reqs;  // answer in [lo, hi)
@@ -51,12 +68,38 @@ info_kernel(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
 hipError_t launch_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
                        const int32_t* seg_indptr, const int32_t* weight_indices,
                        const int32_t* lora_ranks, int32_t* adapter_enabled,
-                       int32_t* token_lora_mapping, hipStream_t stream) {
+                       int32_t* token_lora_mapping, uint32_t* debug_word, hipStream_t stream) {
   int blocks = (int)ceil_div(num_tokens > 0 ? num_tokens : 1, kInfoThreads);
   hipLaunchKernelGGL(info_kernel, dim3(blocks), dim3(kInfoThreads), 0, stream, num_tokens,
                      num_reqs, num_loras, seg_indptr, weight_indices, lora_ranks,
-                     adapter_enabled, token_lora_mapping);
+                     adapter_enabled, token_lora_mapping, debug_word);
   return hipGetLastError();
 }
+
+#ifdef MOE_LORA_DEBUG
+// the precondition flag word of debug builds (one per device)
+__device__ uint32_t g_debug_flags;
+
+uint32_t* debug_word() {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_debug_flags)) != hipSuccess) return nullptr;
+  return static_cast<uint32_t*>(p);
+}
+
+hipError_t debug_word_read(uint32_t* flags, bool clear, hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_debug_flags), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice);
+}
+#else
+uint32_t* debug_word() { return nullptr; }
+hipError_t debug_word_read(uint32_t* flags, bool, hipStream_t) {
+  *flags = 0;
+  return hipErrorNotSupported;
+}
+#endif
 
 }  // namespace moelora

@@ -24,10 +24,16 @@ inline int64_t align_capacity(int64_t P, int64_t E, int64_t L, int64_t BM) {
   return (rows + BM - 1) / BM * BM;
 }
 
+// debug_word: the device flag word of MOE_LORA_DEBUG builds (null: no checks)
 hipError_t launch_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras,
                        const int32_t* seg_indptr, const int32_t* weight_indices,
                        const int32_t* lora_ranks, int32_t* adapter_enabled,
-                       int32_t* token_lora_mapping, hipStream_t stream);
+                       int32_t* token_lora_mapping, uint32_t* debug_word, hipStream_t stream);
+
+// The device flag word of this build on the current device (null in release
+// builds), and reading / clearing it after a stream synchronisation.
+uint32_t* debug_word();
+hipError_t debug_word_read(uint32_t* flags, bool clear, hipStream_t stream);
 
 int route_max_k();
 hipError_t launch_route(int32_t T, int32_t E, int32_t k, const float* logits, int32_t* topk_ids,
@@ -37,7 +43,7 @@ hipError_t launch_align(int32_t T, int32_t k, int32_t E, int32_t L, int32_t BM,
                         const int32_t* topk_ids, const int32_t* mapping, const int32_t* enabled,
                         int32_t* sorted_ids, int32_t* tile_expert, int32_t* tile_lora,
                         int32_t* expert_tile_offsets, int32_t* num_rows_padded, void* workspace,
-                        hipStream_t stream);
+                        uint32_t* debug_word, hipStream_t stream);
 
 // ---- forward ---------------------------------------------------------------
 // expert weights as fp8 e4m3 codes with 128 x 128 block scales (dtype bf16)

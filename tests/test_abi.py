@@ -275,3 +275,20 @@ def test_dense_ctypes_signatures_return_size_t():
                                                                  out0=2048, out1=0, a1=None,
                                                                  b1=None)))
     assert big > (1 << 34)
+
+
+def test_release_build_has_no_debug_checks():
+    """moe_lora_debug_flags exists in every build; a release build reports
+    UNSUPPORTED (and 0) without touching a device."""
+    lib = binding.lib()
+    v = ctypes.c_uint32(77)
+    assert lib.moe_lora_debug_flags(ctypes.byref(v), 1, None) == binding.ERR_UNSUPPORTED
+    assert v.value == 0
+    assert lib.moe_lora_debug_flags(None, 1, None) == binding.ERR_INVALID
+
+
+def test_debug_build_exports_every_declared_symbol():
+    dl = binding.debug_lib()
+    missing = [n for n in _declared_functions() if not hasattr(dl, n)]
+    assert not missing, missing
+
