@@ -302,6 +302,28 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
                             void* const* events);
 
 /*
+ * moe_lora_forward_noalloc -- moe_lora_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, with the
+ * workspace taken from a static device array of the library instead of
+ * args->workspace (workspace and workspace_bytes are ignored).  The call itself
+ * allocates nothing.
+ *   - The array holds moe_lora_forward_noalloc_max_workspace_bytes() bytes
+ *     (64 MiB), one per device, from the library's load until the process
+ *     ends.  A problem whose moe_lora_forward_workspace_bytes exceeds it
+ *     returns MOE_LORA_ERR_WORKSPACE and launches nothing.
+ *   - Every call on a device shares that device's array: calls that overlap
+ *     on one device (two streams, or host threads) race; serialise them.  The
+ *     kernels initialise everything they read, so the previous call's
+ *     contents never matter.
+ *   - Its device address is looked up on the first call on each device
+ *     (hipGetSymbolAddress, with that device current); MOE_LORA_ERR_HIP if
+ *     that fails.  Other errors as for moe_lora_forward.
+ */
+int moe_lora_forward_noalloc(const moe_lora_forward_args* args, void* stream);
+size_t moe_lora_forward_noalloc_max_workspace_bytes(void);
+
+/*
  * Dense projection with per-request LoRA and a two-slice output (LoRA on a
  * fused projection with outputs of unequal sizes: the SGLang PR #22323
  * page, sections 功能与动机 and 实现拆解 item 2 -- the fused q_a_proj +

@@ -104,6 +104,10 @@ def _load(path: str) -> ctypes.CDLL:
     L.moe_lora_dense_forward_events.restype = ctypes.c_int
     L.moe_lora_dense_forward_events.argtypes = [ctypes.POINTER(DenseArgs), ctypes.c_void_p,
                                                 ctypes.POINTER(ctypes.c_void_p)]
+    L.moe_lora_forward_noalloc.restype = ctypes.c_int
+    L.moe_lora_forward_noalloc.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.c_void_p]
+    L.moe_lora_forward_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_lora_forward_noalloc_max_workspace_bytes.argtypes = []
     L.moe_lora_debug_flags.restype = ctypes.c_int
     L.moe_lora_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                        ctypes.c_void_p]
@@ -397,6 +401,30 @@ def moe_lora_forward(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: tor
         _check(lib().moe_lora_forward_events(ctypes.byref(a), _stream(), arr),
                "moe_lora_forward_events")
     return y
+
+
+def moe_lora_forward_noalloc(x: torch.Tensor, topk_weights: torch.Tensor, w_gate_up: torch.Tensor,
+                             w_down: torch.Tensor, align_out: Dict[str, torch.Tensor], top_k: int,
+                             lora_ranks: Optional[torch.Tensor] = None,
+                             scaling: Optional[torch.Tensor] = None,
+                             pools: Optional[Dict[str, torch.Tensor]] = None,
+                             y: Optional[torch.Tensor] = None, out_dtype=None,
+                             w_scales=None) -> torch.Tensor:
+    """moe_lora_forward without a caller workspace: the library's static
+    per-device scratch serves instead (problems up to
+    ``moe_lora_forward_noalloc_max_workspace_bytes()``; calls on one device must
+    not overlap).  Only ``y`` is allocated here, and only when not given."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype if out_dtype is None else out_dtype,
+                        device=x.device)
+    a = _forward_args(x, topk_weights, w_gate_up, w_down, align_out, lora_ranks, scaling, pools,
+                      top_k, y, None, out_dtype, w_scales)
+    _check(lib().moe_lora_forward_noalloc(ctypes.byref(a), _stream()), "moe_lora_forward_noalloc")
+    return y
+
+
+def moe_lora_forward_noalloc_max_workspace_bytes() -> int:
+    return int(lib().moe_lora_forward_noalloc_max_workspace_bytes())
 
 
 def run_layer(inputs: dict, block_m: int = 16, with_lora: bool = True,

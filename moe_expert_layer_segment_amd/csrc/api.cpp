@@ -206,6 +206,23 @@ int moe_lora_forward_events(const moe_lora_forward_args* args, void* stream,
   return forward_impl(args, stream, events);
 }
 
+int moe_lora_forward_noalloc(const moe_lora_forward_args* args, void* stream) {
+  ForwardProblem p;
+  // the workspace fields are not used: validate as if a workspace were given
+  int st = to_problem(args, &p, false);
+  if (st != MOE_LORA_OK) return st;
+  if (p.T == 0) return MOE_LORA_OK;
+  moe_lora_forward_args chk = *args;
+  chk.workspace = reinterpret_cast<void*>(uintptr_t(256));
+  st = to_problem(&chk, &p, true);
+  if (st != MOE_LORA_OK) return st;
+  if (forward_ws_layout(p).bytes > kNoAllocScratchBytes) return MOE_LORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess || !ws) return MOE_LORA_ERR_HIP;
+  return hip_status(launch_forward(p, ws, static_cast<hipStream_t>(stream), nullptr));
+}
+
+size_t moe_lora_forward_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
 
 static int to_dense(const moe_lora_dense_args* a, DenseProblem* p, bool check_ptrs) {
   if (!a || a->struct_size < sizeof(moe_lora_dense_args)) return MOE_LORA_ERR_INVALID;

@@ -16,6 +16,8 @@
 //   combine  -- y[t] = sum_j z[t*k + j] for j = 0..k-1 in order (fp32), cast to dtype.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1891,5 +1893,36 @@ hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t 
   return run_forward<float>(p, workspace, stream, events);
 }
 
+// --------------------------------------------------------------------------
+// the static workspace of the allocation-free forward entry point
+// --------------------------------------------------------------------------
+// One array per device, held from the library's load until the process ends.
+// Host code never passes the array's name to a kernel (in host code it is only
+// a stand-in for the device symbol): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace moelora

@@ -82,6 +82,11 @@ enum { kStagePlan = 0, kStageShrinkX, kStageGateUp, kStageShrinkA, kStageDown, k
 hipError_t launch_forward(const ForwardProblem& p, void* workspace, hipStream_t stream,
                           hipEvent_t* events);
 
+// The allocation-free forward's workspace: a static device array of this many
+// bytes, one per device; noalloc_scratch returns the current device's address.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // A dense projection with per-request LoRA whose output is two column slices
 // [0, N0) and [N0, N0 + N1), each with its own LoRA factors (N1 may be 0).
 struct DenseProblem {

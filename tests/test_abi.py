@@ -292,3 +292,18 @@ def test_debug_build_exports_every_declared_symbol():
     missing = [n for n in _declared_functions() if not hasattr(dl, n)]
     assert not missing, missing
 
+
+def test_noalloc_forward_refuses_oversized_problems():
+    """The allocation-free forward serves problems whose workspace fits its
+    static scratch; a larger one is refused before any device call."""
+    lib = binding.lib()
+    cap = lib.moe_lora_forward_noalloc_max_workspace_bytes()
+    assert cap == 64 << 20
+    big = _fargs(num_tokens=4096, hidden=4096, inter=14336, num_experts=8)
+    assert lib.moe_lora_forward_workspace_bytes(ctypes.byref(big)) > cap
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(big), None) == binding.ERR_WORKSPACE
+    # argument errors come first, as for moe_lora_forward; the workspace fields are ignored
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(_fargs(dtype=7)), None) == binding.ERR_UNSUPPORTED
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(_fargs(x=None)), None) == binding.ERR_INVALID
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(_fargs(x=0x1008)), None) == binding.ERR_INVALID
+    assert lib.moe_lora_forward_noalloc(ctypes.byref(_fargs(num_tokens=0, workspace=None)), None) == binding.OK
