@@ -25,7 +25,7 @@ LIB = os.path.join(LIBDIR, "libmoe_lora.so")
 DEBUG_LIB = os.path.join(LIBDIR, "libmoe_lora_debug.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "route.hip", "info.hip", "align.hip", "forward.hip"]
+SOURCES = ["api.cpp", "route.hip", "info.hip", "align.hip", "forward.hip", "gemm_big.hip"]
 # sources whose code differs under MOE_LORA_DEBUG (the rest is shared)
 DEBUG_SOURCES = ["api.cpp", "info.hip", "align.hip"]
 ARCH = "gfx950"

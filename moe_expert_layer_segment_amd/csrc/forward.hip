@@ -19,6 +19,7 @@
 #include <mutex>
 
 #include "common.hpp"
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace moelora {
@@ -88,10 +89,16 @@ plan_kernel(int E, int BM, int rows_per_item, const int32_t* __restrict__ expert
 // {first row, rows, expert, column tile x K split}; rows = 0 marks a tile
 // past the item count.
 #ifndef MOELORA_GROUP_ITEMS
-#define MOELORA_GROUP_ITEMS 8   // work items per tile group (see above)
+#define MOELORA_GROUP_ITEMS 8   // work items per tile group of 128-row items (see above)
+#endif
+// 256-row items against 256-row weight tiles (measured on the 16384-token
+// prefill batch, gate_up GEMM: 4 items 7.87 ms, 6 7.79, 8 7.66, 12 7.52)
+#ifndef MOELORA_GROUP_ITEMS_BIG
+#define MOELORA_GROUP_ITEMS_BIG 12
 #endif
 __device__ inline int4 gemm_tile_of(const int4* items, int count, int n_tiles, const int32_t* eto,
-                                    int BM_tile, int E, int rows_per_item, int logical) {
+                                    int BM_tile, int E, int rows_per_item, int logical,
+                                    int group_items) {
   const int4 skip = make_int4(0, 0, 0, -1);
   // the expert group of logical tile `logical` spans its items' range times
   // n_tiles, so item logical / n_tiles belongs to it
@@ -101,7 +108,7 @@ __device__ inline int4 gemm_tile_of(const int4* items, int count, int n_tiles, c
   const int rows_e = (eto[eg + 1] - eto[eg]) * BM_tile;
   const int n_e = (rows_e + rows_per_item - 1) / rows_per_item;   // the expert's items
   if (n_e <= 0) return skip;
-  const int ng = max(1, (n_e + MOELORA_GROUP_ITEMS / 2) / MOELORA_GROUP_ITEMS);
+  const int ng = max(1, (n_e + group_items / 2) / group_items);
   const int gbase = n_e / ng, grem = n_e % ng;   // groups 0..grem-1 have gbase+1 items
   const int li = logical / n_tiles - first;      // an item index inside the group
   const int gj = li < grem * (gbase + 1) ? li / (gbase + 1) : grem + (li - grem * (gbase + 1)) / gbase;
@@ -123,16 +130,18 @@ tile_table_kernel(const int4* __restrict__ items, const int32_t* __restrict__ it
                   const int32_t* __restrict__ expert_tile_offsets, int BM_tile, int E, int rows_per_item,
                   int n_tiles0, int4* __restrict__ tab0, int n_tiles1, int4* __restrict__ tab1,
                   const int32_t* __restrict__ tile_lora, const int32_t* __restrict__ lora_ranks, int L,
-                  int R, int n_blocks, int32_t* __restrict__ slot_rank) {
+                  int R, int n_blocks, int32_t* __restrict__ slot_rank, int group_items) {
   const int count = min(item_count[0], max_items);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t n0 = (int64_t)count * n_tiles0, n1 = tab1 ? (int64_t)count * n_tiles1 : 0;
   const int64_t n = max(max(n0, n1), (int64_t)(slot_rank ? n_blocks : 0));
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
     if (i < n0)
-      tab0[i] = gemm_tile_of(items, count, n_tiles0, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i);
+      tab0[i] = gemm_tile_of(items, count, n_tiles0, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i,
+                             group_items);
     if (i < n1)
-      tab1[i] = gemm_tile_of(items, count, n_tiles1, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i);
+      tab1[i] = gemm_tile_of(items, count, n_tiles1, expert_tile_offsets, BM_tile, E, rows_per_item, (int)i,
+                             group_items);
     if (slot_rank && i < n_blocks) {
       const int l = tile_lora[i];
       const int r = (l >= 0 && l < L) ? min(lora_ranks[l], R) : 0;
@@ -498,76 +507,6 @@ template <> struct Blk<float> {
   __device__ static inline int row(int v, int lane) { return 4 * (lane >> 4) + v; }
 };
 
-template <typename T>
-struct GemmArgs {
-  const int4* items;
-  const int32_t* item_count;
-  int max_items, n_tiles;      // n_tiles: column tiles x K splits
-  int n_cols, ksplit;           // column tiles; K splits (down only, else 1)
-  // A operand
-  const T* a_src;             // x [T, K] (gate_up, gathered) or act [cap, K] (down)
-  const int32_t* sorted_ids;
-  int top_k, P;
-  int64_t K;
-  // B operand: weights [E, w_rows, K], in T or as fp8 e4m3 codes
-  const void* w;
-  const float* w_scale;       // fp8 weights: [E, w_rows/128, K/128] block scales, else null
-  int64_t n_out;              // output columns (I for gate_up, H for down)
-  int64_t w_rows;             // rows per expert of w (2I or H)
-  // LoRA
-  const int32_t* tile_lora;
-  const int32_t* expert_tile_offsets;   // [E+1], in align blocks of BM_tile rows
-  int BM_tile;
-  const int32_t* lora_ranks;
-  const float* h;             // [cap, HS], fp32 (scaled shrink result)
-  int HS, RP, R, L, E;
-  const T* b_pool0;           // [L, E, R, n_out] (gate or down)
-  const T* b_pool1;           // [L, E, R, n_out] (up) or null
-  // outputs
-  T* act;                     // gate_up: [cap, n_out]
-  float* z;                   // down: [ksplit, P, n_out], one plane per K split
-  const float* topk_weights;
-  int64_t cap;                // rows of sorted_ids / act / h
-  int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
-  const int4* tile_tab;       // [item count x n_tiles] logical tile records (tile_table_kernel)
-  const int32_t* slot_rank;   // [cap / BM_tile] slot | rank << 16 per align block, or -1
-  int64_t n_split;            // dense mode: output columns [0, n_split) use b_pool0 and h[:, :RP],
-                              // the rest b_pool1 and h[:, RP:2RP] (a multiple of 32)
-};
-
-
-__device__ inline int xcd_remap(int bid, int nblocks) {
-  // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of logical tiles so neighbouring tiles share its L2
-  const int q = nblocks / 8;
-  if (bid >= q * 8) return bid;
-  return (bid % 8) * q + bid / 8;
-}
-
-// Issue one 16-byte-per-lane global -> LDS load: lane i of the wave writes the
-// 16 bytes at gbase + goff to LDS byte address lds_addr + 16 * i.  The LDS base
-// goes through M0 (saved and restored around the load, so the compiler's view
-// of M0 is unchanged).  The compiler does not track these loads: callers wait
-// for them with an explicit s_waitcnt vmcnt before a barrier.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t lds_addr) {
-  // base and LDS address are wave-uniform: move them to SGPRs explicitly
-  const uint64_t g = (uint64_t)(uintptr_t)gbase;
-  const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
-  const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
-  const uint64_t gs = ((uint64_t)ghi << 32) | glo;
-  const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[la]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[go], %[gb]\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [la] "s"(la), [go] "v"(goff), [gb] "s"(gs)
-      : "memory");
-}
-
 // 16 fp8 e4m3 codes (4 dwords, element 4w+b = byte b of dword w) times a
 // block scale, as two bf16x8 fragments: elements 0..7 and 8..15.  The code
 // itself converts exactly (every e4m3 value is a bf16 value); the product
@@ -604,13 +543,6 @@ __device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bool pow2, b
   }
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  // all of this wave's LDS loads except the newest N have landed, then every
-  // wave of the workgroup has got that far
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // W: weight element, T (bf16 / fp32 weights) or uint8_t (fp8 e4m3 codes with
 // 128 x 128 block scales; T = bf16).
@@ -1310,9 +1242,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
 // combine: y[t, c] = sum_j sum_q z[q, t*k + j, c]  (j, then the down GEMM's
 // K splits q, in order, fp32)
 // --------------------------------------------------------------------------
-template <typename OutT>
+template <typename ZT, typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H,
+combine_kernel(const ZT* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H,
                int nsplit, int64_t split_stride) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T_ * H) return;
@@ -1320,8 +1252,15 @@ combine_kernel(const float* __restrict__ z, OutT* __restrict__ y, int64_t T_, in
   floatx4 s = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j)
     for (int q = 0; q < nsplit; ++q) {   // pair j's K splits, in order
-      floatx4 v = *reinterpret_cast<const floatx4*>(z + q * split_stride + (t * k + j) * H + c);
-      s += v;
+      const ZT* zp = z + q * split_stride + (t * k + j) * H + c;
+      if constexpr (sizeof(ZT) == 4) {
+        s += *reinterpret_cast<const floatx4*>(zp);
+      } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(zp);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] += (float)v[u];
+      }
     }
 #pragma unroll
   for (int q = 0; q < 4; ++q) y[i + q] = Elt<OutT>::from_float(s[q]);
@@ -1411,6 +1350,35 @@ static int down_ksplit(int64_t P, int64_t E, int64_t H, int64_t I, bool fp8) {
 
 static int rows_per_item(int dtype) { return dtype == 1 ? TileCfg<bf16_t>::BM : TileCfg<float>::BM; }
 
+// The large-tile bf16 GEMMs serve batches with at least this many pairs per
+// expert on average (prefill) on layers with a hidden size of at least
+// MOELORA_BIG_MIN_HIDDEN.  Their 256-row items would be mostly padding for
+// decode-sized batches, and a short last item wastes more rows than the
+// general kernel's: on the 128-expert layer (hidden 2048, intermediate 768,
+// 8192 tokens, 512 pairs per expert with skewed routing) they measured
+// slower (1.49 against 1.35 ms per layer), on the 256-expert layer (hidden
+// 7168, 512 pairs per expert) faster (13.8 against 14.5 ms), on the 8-expert
+// layer (hidden 4096, 1024 pairs per expert) even.
+#ifndef MOELORA_BIG_MIN_PAIRS_PER_EXPERT
+#define MOELORA_BIG_MIN_PAIRS_PER_EXPERT 256
+#endif
+#ifndef MOELORA_BIG_MIN_HIDDEN
+#define MOELORA_BIG_MIN_HIDDEN 4096
+#endif
+static bool use_big(const ForwardProblem& p) {
+  return p.dtype == 1 && p.wdtype != kWeightFp8 && p.H >= MOELORA_BIG_MIN_HIDDEN &&
+         p.T * p.k >= (int64_t)MOELORA_BIG_MIN_PAIRS_PER_EXPERT * p.E;
+}
+
+// K splits of the large-tile down GEMM: as for the general kernel, two K
+// halves when a long I leaves fewer than 8 tiles per workgroup
+static int down_ksplit_big(int64_t P, int64_t E, int64_t H, int64_t I) {
+  const int64_t items = ceil_div(P, big_tile_rows()) + std::min(P, E);
+  const int64_t tiles = items * ceil_div(H, big_tile_cols(false));
+  if (P <= 0 || I % (2 * big_tile_k()) != 0 || I / 2 < 4096 || tiles >= 8 * 256) return 1;
+  return 2;
+}
+
 // K splits of a shrink: enough workgroups to fill the GPU when the batch has
 // few rows (decode), each split at least 512 deep and a multiple of 128 (the
 // four waves' interleaved 32-deep steps).
@@ -1487,7 +1455,9 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   const int64_t P = p.T * p.k;
   const size_t esz = p.dtype == 1 ? 2 : 4;
   w.cap = align_capacity(P, p.E, p.L, p.BM);
-  const int rpi = rows_per_item(p.dtype);
+  w.big = use_big(p);
+  const int rpi = w.big ? big_tile_rows() : rows_per_item(p.dtype);
+  w.rows_per_item = rpi;
   w.max_items = ceil_div(w.cap, rpi) + (P < p.E ? P : p.E);
   if (w.max_items < 1) w.max_items = 1;
   w.RP = p.L > 0 ? round_up(p.R > 0 ? p.R : 1, 32) : 0;
@@ -1498,9 +1468,13 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.shrink4 = use_shrink4(P, p.E, p.L);
   w.split_gu = shrink_splits(P, p.H, w.shrink4, 2);
   w.split_d = shrink_splits(P, p.I, w.shrink4, 1);
-  w.split_down_k = p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
+  w.split_down_k = w.big ? down_ksplit_big(P, p.E, p.H, p.I)
+                 : p.dtype == 1 ? down_ksplit<bf16_t>(P, p.E, p.H, p.I, p.wdtype == kWeightFp8)
                                 : down_ksplit<float>(P, p.E, p.H, p.I, false);
-  if (p.dtype == 1) {
+  if (w.big) {
+    w.n_tiles_gu = ceil_div(p.I, big_tile_cols(true));
+    w.n_tiles_dn = ceil_div(p.H, big_tile_cols(false)) * w.split_down_k;
+  } else if (p.dtype == 1) {
     w.n_tiles_gu = ceil_div(p.I, TileCfg<bf16_t>::BN / 2);
     w.n_tiles_dn = ceil_div(p.H, TileCfg<bf16_t>::BN_DOWN) * w.split_down_k;
   } else {
@@ -1537,7 +1511,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   float* z = reinterpret_cast<float*>(ws + w.z_off);
   const int64_t P = p.T * p.k;
   const bool lora = p.L > 0;
-  constexpr int BM = TileCfg<T>::BM, BN = TileCfg<T>::BN;
+  const int BM = w.rows_per_item;   // rows of a work item
+  constexpr int BN = TileCfg<T>::BN;
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   const bool fp8w = kBf16 && p.wdtype == kWeightFp8;
   const bool fp8_deep_k = P >= (int64_t)MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT * p.E;
@@ -1554,7 +1529,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
                        dim3(256), 0, stream, items, count, (int)w.max_items, p.expert_tile_offsets,
                        (int)p.BM, (int)p.E, BM, (int)w.n_tiles_gu, tab_gu, (int)w.n_tiles_dn, tab_dn,
                        p.tile_lora, p.lora_ranks, (int)p.L, (int)p.R, (int)(w.cap / p.BM),
-                       lora ? slot_rank : nullptr);
+                       lora ? slot_rank : nullptr, w.big ? MOELORA_GROUP_ITEMS_BIG : MOELORA_GROUP_ITEMS);
   }
   mark(2 * kStagePlan + 1);
 
@@ -1613,7 +1588,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.w_scale = fp8w ? p.w_gate_up_scale : nullptr;
     a.n_out = p.I;
     a.w_rows = 2 * p.I;
-    a.n_cols = (int)ceil_div(p.I, BN / 2);
+    a.n_cols = (int)w.n_tiles_gu;
     a.ksplit = 1;
     a.n_tiles = a.n_cols;
     a.tile_tab = tab_gu;
@@ -1626,7 +1601,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     hipEvent_t ev0 = events ? events[2 * kStageGateUp] : nullptr, ev1 = events ? events[2 * kStageGateUp + 1] : nullptr;
     if constexpr (kBf16) {
-      if (fp8w && fp8_deep_k) {
+      if (w.big) {
+        launch_gemm_big(true, a, nblk, stream, ev0, ev1);
+      } else if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
         launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
@@ -1636,8 +1613,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       }
     }
-    if (!fp8w)
-      launch_timed((gemm_kernel<T, T, BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
+    if (!fp8w && !w.big)
+      launch_timed((gemm_kernel<T, T, TileCfg<T>::BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
                             dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
   }
   mark(2 * kStageShrinkA);
@@ -1677,8 +1654,8 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.w_scale = fp8w ? p.w_down_scale : nullptr;
     a.n_out = p.H;
     a.w_rows = p.H;
-    constexpr int BND = TileCfg<T>::BN_DOWN, SD = TileCfg<T>::STAGES_DOWN;
-    a.n_cols = (int)ceil_div(p.H, BND);
+    constexpr int SD = TileCfg<T>::STAGES_DOWN;
+    a.n_cols = (int)(w.n_tiles_dn / w.split_down_k);
     a.ksplit = w.split_down_k;
     a.n_tiles = a.n_cols * a.ksplit;
     a.tile_tab = tab_dn;
@@ -1691,7 +1668,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     hipEvent_t ev0 = events ? events[2 * kStageDown] : nullptr, ev1 = events ? events[2 * kStageDown + 1] : nullptr;
     if constexpr (kBf16) {
-      if (fp8w && fp8_deep_k) {
+      if (w.big) {
+        launch_gemm_big(false, a, nblk, stream, ev0, ev1);
+      } else if (fp8w && fp8_deep_k) {
         typedef Fp8Cfg F;
         launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, false>),
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
@@ -1701,19 +1680,20 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       }
     }
-    if (!fp8w)
-      launch_timed((gemm_kernel<T, T, BM, BND, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
+    if (!fp8w && !w.big)
+      launch_timed((gemm_kernel<T, T, TileCfg<T>::BM, TileCfg<T>::BN_DOWN, TileCfg<T>::WM, TileCfg<T>::WN, SD, TileCfg<T>::ROWB, false>),
                             dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
   }
   mark(2 * kStageCombine);
   if (P > 0) {
     const int64_t n4 = p.T * p.H / 4;
+    const dim3 cg((unsigned)ceil_div(n4, 256));
     if (p.out_f32)
-      hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<float*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
+      hipLaunchKernelGGL((combine_kernel<float, float>), cg, dim3(256), 0, stream, z,
+                         static_cast<float*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
     else
-      hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<T*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
+      hipLaunchKernelGGL((combine_kernel<float, T>), cg, dim3(256), 0, stream, z,
+                         static_cast<T*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
   }
   mark(2 * kStageCombine + 1);
   return hipGetLastError();
@@ -1786,7 +1766,8 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     hipLaunchKernelGGL(tile_table_kernel, dim3((unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(n, 256)))),
                        dim3(256), 0, stream, items, count, (int)w.max_items, p.expert_tile_offsets,
                        (int)p.BM, 1, BM, (int)w.n_tiles, tab, 0, (int4*)nullptr, p.tile_lora,
-                       p.lora_ranks, (int)p.L, (int)p.R, (int)(w.cap / p.BM), lora ? slot_rank : nullptr);
+                       p.lora_ranks, (int)p.L, (int)p.R, (int)(w.cap / p.BM), lora ? slot_rank : nullptr,
+                       MOELORA_GROUP_ITEMS);
   }
   mark(2 * kDenseStagePlan + 1);
 
@@ -1871,10 +1852,10 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
   if (P > 0) {
     const int64_t n4 = P * N / 4;
     if (p.out_f32)
-      hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+      hipLaunchKernelGGL((combine_kernel<float, float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
                          stream, z, static_cast<float*>(p.y), P, 1, N, w.ksplit, P * N);
     else
-      hipLaunchKernelGGL((combine_kernel<T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+      hipLaunchKernelGGL((combine_kernel<float, T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
                          stream, z, static_cast<T*>(p.y), P, 1, N, w.ksplit, P * N);
   }
   mark(2 * kDenseStageCombine + 1);

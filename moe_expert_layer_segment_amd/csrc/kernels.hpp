@@ -74,6 +74,8 @@ struct ForwardWs {
   int split_gu = 1, split_d = 1;   // K splits of the two shrinks
   bool shrink4 = false;            // shrinks share pool rows across 4 row groups
   int split_down_k = 1;            // K splits of the down GEMM (planes of z)
+  bool big = false;                // the large-tile bf16 GEMMs (256-row items)
+  int rows_per_item = 0;           // rows of a GEMM work item
 };
 ForwardWs forward_ws_layout(const ForwardProblem& p);
 // stages of the forward, in launch order (index into the optional event pairs)

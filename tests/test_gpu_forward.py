@@ -8,9 +8,9 @@ The full-size runs use the launch configuration the benchmark times.
 The tolerance is applied to the fp32 combine result (out_dtype=float32): a
 bf16 y carries up to half an ulp of final rounding (0.0625 for |y| >= 16),
 which alone can exceed the 5e-2 max-abs bar.  The bf16 output itself is then
-checked to be exactly the round-to-nearest-even of that fp32 result, and is
-also held to the bar directly (the workloads' outputs stay well below 16 in
-magnitude, where half a bf16 ulp is at most 0.03).
+checked to be exactly the round-to-nearest-even of that fp32 result; for the
+configured workloads it is also held to the bar directly (their outputs stay
+small enough that the final rounding leaves room inside the bar).
 """
 import numpy as np
 import pytest
@@ -39,10 +39,13 @@ def _y(inp, **kw):
     return to_np(y32)
 
 
-def _check(got, ref, dtype, what, rows=None):
-    """The bar on the fp32 combine result, and for bf16 also on the bf16 y."""
+def _check(got, ref, dtype, what, rows=None, bf16_y=False):
+    """The bar on the fp32 combine result; with ``bf16_y`` (the configured
+    workloads) also on the bf16 y itself.  Synthetic small layers with rank-64
+    deltas reach |y| >= 8, where half a bf16 ulp (0.03) plus the kernel's own
+    error can pass 5e-2, so there only the fp32 result is held to the bar."""
     assert_layer_close(got if rows is None else got[rows], ref, dtype, what)
-    if "y" in _LAST_BF16:
+    if bf16_y and "y" in _LAST_BF16:
         y16 = _LAST_BF16["y"] if rows is None else _LAST_BF16["y"][rows]
         assert_layer_close(y16, ref, dtype, what + " [bf16 y]")
 
@@ -102,6 +105,15 @@ SMALL = [
     ("bf16_no_lora_slots", 8, 2, 128, 128, 2, [0, 0], [30, 30], [0, 1], "bf16", 8),
     ("f32_tiles", 8, 2, 128, 192, 3, [4, 0, 16], [20, 13, 60], [2, 1, 0], "f32", 16),
     ("f32_ragged", 5, 2, 64, 320, 2, [16, 7], [9, 70], [-1, 1], "f32", 16),
+    # hidden >= 4096 and >= 256 pairs per expert: the large-tile bf16 GEMMs
+    # (256-row items; partial last items, ragged output columns, rank 64)
+    ("big_two_experts", 2, 2, 4096, 384, 4, [0, 8, 16, 16], [200, 1, 77, 3, 190, 29],
+     [2, 0, 3, 2, -1, 1], "bf16", 16),
+    ("big_ragged_rank64", 3, 2, 4160, 320, 5, [64, 0, 8, 64, 33], [300, 120, 9, 250],
+     [0, 4, 3, -1], "bf16", 64),
+    ("big_one_expert_partial", 1, 1, 4096, 256, 2, [32, 16], [161, 130], [1, 0], "bf16", 32),
+    ("big_many_slots", 4, 2, 4096, 192, 8, [8, 16, 24, 32, 8, 16, 24, 32],
+     [70, 60, 50, 90, 80, 40, 60, 70, 30, 20], [0, 1, 2, 3, 4, 5, 6, 7, 0, -1], "bf16", 32),
 ]
 
 
@@ -126,7 +138,7 @@ def test_full_size_every_token(name):
     got = _y(inp)
     assert np.all(np.isfinite(got))
     ref = oracle_forward(inp)
-    _check(got, ref, spec.dtype, f"{name} (all {spec.num_tokens} tokens)")
+    _check(got, ref, spec.dtype, f"{name} (all {spec.num_tokens} tokens)", bf16_y=True)
     del inp
     torch.cuda.empty_cache()
 
@@ -141,7 +153,7 @@ def test_full_size_c4p_boundaries():
     got = _y(inp)
     assert np.all(np.isfinite(got))
     ref = oracle_forward(inp, tokens=sample)
-    _check(got, ref, spec.dtype, f"c4p ({len(sample)} tokens)", rows=sample)
+    _check(got, ref, spec.dtype, f"c4p ({len(sample)} tokens)", rows=sample, bf16_y=True)
     del inp
     torch.cuda.empty_cache()
 
@@ -171,6 +183,17 @@ def test_random_shapes(seed):
     got = _y(inp, with_lora=L > 0)
     ref = oracle_forward(inp, with_lora=L > 0)
     _check(got, ref, dt, spec.name)
+
+
+def test_big_tile_down_k_split():
+    """The large-tile down GEMM with its K split in two (I >= 8192, few tiles):
+    two bf16 planes of z added in order by the combine."""
+    spec = workloads.LayerSpec("big_ksplit", 1, 1, 4096, 8192, 2, [16, 8], [300, 60, 190],
+                               [0, -1, 1], seed=29, pool_rank=16)
+    say("forward large tiles with the down K split (I = 8192)")
+    inp = gpu_inputs(spec)
+    got = _y(inp)
+    _check(got, oracle_forward(inp), "bf16", spec.name)
 
 
 def test_reductions_to_base():
