@@ -53,20 +53,22 @@ def parse():
                          "the reference kernel that scales FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="host only: read the rocprofv3 counter CSVs under DIR/{fetch,write,"
-                         "cfetch,cwrite}, write the calibrated per-launch HBM traffic of every "
-                         "layer kernel of --config to --traffic and exit")
+                         "cfetch,cwrite} (and, when present, DIR/mfma and DIR/tcc), write the "
+                         "calibrated per-launch HBM traffic, MFMA utilisation and L2 hit rate of "
+                         "every layer kernel of --config to --traffic and exit")
     return ap.parse_args()
 
 
 # kernel name (rocprofv3, mangled or not) -> forward stage or metadata kernel
 def _stage_of(kname):
-    if "gemm_kernel" in kname:
+    if "gemm_kernel" in kname or "gemm_big_kernel" in kname:
         gate_up = ("Lb1E" in kname) or kname.rstrip(") ").split("(")[0].endswith("true>")
         return "gate_up_gemm" if gate_up else "down_gemm"
     if "shrink_reduce" in kname:
         return "shrink_reduce"
-    if "shrink_kernel" in kname:
-        return "shrink_gate_up" if ("Li2E" in kname or ", 2>" in kname) else "shrink_down"
+    if "shrink_kernel" in kname or "shrink4_kernel" in kname:
+        return "shrink_gate_up" if ("Li2E" in kname or ", 2>" in kname or ", 2," in kname) \
+            else "shrink_down"
     for key in ("combine", "plan", "tile_table", "info", "align_count", "align_scan", "align_scatter"):
         if key + "_kernel" in kname:
             return key
@@ -119,6 +121,27 @@ def traffic_from_counters(args):
         wb = float(np.mean(wv)) * w_scale * 1024
         stages[st] = dict(bytes=round(fb + wb), fetch_bytes=round(fb), write_bytes=round(wb),
                           dispatches=len(vals))
+
+    def optional(sub, counter):
+        path = os.path.join(args.traffic_from, sub, "run_counter_collection.csv")
+        return per_kernel(sub, counter) if os.path.exists(path) else {}
+
+    # MFMA utilisation: MFMA-busy cycles summed over the 1024 SIMDs against the
+    # GPU-active cycles (GRBM_GUI_ACTIVE, summed over the 8 XCDs) of the dispatch
+    busy, active = optional("mfma", "SQ_VALU_MFMA_BUSY_CYCLES"), optional("mfma", "GRBM_GUI_ACTIVE")
+    for kname, vals in busy.items():
+        st = _stage_of(kname)
+        if st in stages and kname in active:
+            cyc = float(np.mean(active[kname])) / 8
+            stages[st]["mfma_busy_frac"] = round(float(np.mean(vals)) / (cyc * 1024), 4)
+            stages[st]["gpu_cycles"] = round(cyc)
+    hit, miss = optional("tcc", "TCC_HIT_sum"), optional("tcc", "TCC_MISS_sum")
+    for kname, vals in hit.items():
+        st = _stage_of(kname)
+        if st in stages and kname in miss:
+            h, m = float(np.mean(vals)), float(np.mean(miss[kname]))
+            stages[st]["l2_hit_rate"] = round(h / max(h + m, 1.0), 4)
+            stages[st]["l2_requests"] = round(h + m)
     from moe_expert_layer_segment_amd import workloads
     spec = workloads.config(args.config)
     out = {}
