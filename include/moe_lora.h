@@ -108,7 +108,8 @@ int moe_lora_info(int32_t num_tokens, int32_t num_reqs, int32_t num_loras, int32
  * Capacity (rows) of the align outputs: P + min(P, E*(L+1)) * (block_m - 1)
  * rounded up to block_m, with P = num_tokens * top_k.  sorted_pair_ids needs
  * this many entries; tile_expert / tile_lora need capacity / block_m.
- * Returns -1 for invalid arguments.
+ * Returns -1 for invalid arguments and for sizes moe_lora_align does not
+ * support (P > INT32_MAX / 2 or num_experts * (num_loras + 1) > 32768).
  */
 int64_t moe_lora_align_capacity_rows(int32_t num_tokens, int32_t top_k, int32_t num_experts,
                                      int32_t num_loras, int32_t block_m);

@@ -68,13 +68,17 @@ int64_t moe_lora_align_capacity_rows(int32_t num_tokens, int32_t top_k, int32_t 
                                      int32_t num_loras, int32_t block_m) {
   if (num_tokens < 0 || top_k <= 0 || num_experts <= 0 || num_loras < 0 || bad_block_m(block_m))
     return -1;
-  return align_capacity((int64_t)num_tokens * top_k, num_experts, num_loras, block_m);
+  // sizes align refuses have no capacity (and P, E*(L+1) bounded here keep the
+  // arithmetic below 2^40)
+  const int64_t P = (int64_t)num_tokens * top_k;
+  if (P > INT32_MAX / 2 || (int64_t)num_experts * ((int64_t)num_loras + 1) > kMaxKeys) return -1;
+  return align_capacity(P, num_experts, num_loras, block_m);
 }
 
 size_t moe_lora_align_workspace_bytes(int32_t num_tokens, int32_t top_k, int32_t num_experts,
                                       int32_t num_loras, int32_t block_m) {
   if (moe_lora_align_capacity_rows(num_tokens, top_k, num_experts, num_loras, block_m) < 0) return 0;
-  return align_ws_layout((int64_t)num_tokens * top_k, (int64_t)num_experts * (num_loras + 1)).bytes;
+  return align_ws_layout((int64_t)num_tokens * top_k, (int64_t)num_experts * ((int64_t)num_loras + 1)).bytes;
 }
 
 int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32_t num_loras,
@@ -87,7 +91,7 @@ int moe_lora_align(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32
   if (top_k > num_experts) return MOE_LORA_ERR_INVALID;
   const int64_t P = (int64_t)num_tokens * top_k;
   if (P > INT32_MAX / 2) return MOE_LORA_ERR_UNSUPPORTED;
-  if ((int64_t)num_experts * (num_loras + 1) > kMaxKeys) return MOE_LORA_ERR_UNSUPPORTED;
+  if ((int64_t)num_experts * ((int64_t)num_loras + 1) > kMaxKeys) return MOE_LORA_ERR_UNSUPPORTED;
   if (!expert_tile_offsets || !num_rows_padded) return MOE_LORA_ERR_INVALID;
   if (P > 0 && (!topk_ids || !token_lora_mapping || !sorted_pair_ids || !tile_expert || !tile_lora))
     return MOE_LORA_ERR_INVALID;
