@@ -48,8 +48,8 @@ def test_kernels_use_no_scratch(src, tmp_path):
 def _k_loop_scratch(asm, kernel):
     """Scratch instructions inside the K loop of `kernel` in hipcc -S output:
     of the loops whose body holds the barrier after the all-loads wait, the
-    one with the MFMAs (the other serves waves whose rows all lie past a
-    short item's end)."""
+    innermost one with the MFMAs (another serves waves whose rows all lie past
+    a short item's end, and the persistent tile loop holds them all)."""
     start = asm.index(kernel + ":")
     body = asm[start:asm.index("s_endpgm", start)].split("\n")
     labels = {l.split(":")[0].strip(): i for i, l in enumerate(body) if l.startswith(".LBB")}
@@ -60,8 +60,9 @@ def _k_loop_scratch(asm, kernel):
             if tok and tok[0].startswith("s_cbranch") and tok[-1] in labels and labels[tok[-1]] < bar:
                 loops.append(body[labels[tok[-1]]:i + 1])
                 break
-    k_loop = max(loops, key=lambda lp: sum("v_mfma" in l for l in lp))
-    assert sum("v_mfma" in l for l in k_loop) >= 32, "K loop not found"
+    with_mfma = [lp for lp in loops if sum("v_mfma" in l for l in lp) >= 32]
+    assert with_mfma, "K loop not found"
+    k_loop = min(with_mfma, key=len)
     return sum("scratch_" in l for l in k_loop)
 
 
