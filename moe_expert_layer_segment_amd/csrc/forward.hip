@@ -703,13 +703,23 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   constexpr int NG = BS / 16;
   int lg[MB][NG], rg[MB][NG], p0[MB], r0[MB];
   if (lora_here) {
+    // row numbers fit in 32 bits: a 32-bit divide each, and all the loads go
+    // out before the first is used (a 64-bit divide's branches kept each load
+    // behind the previous one's wait: one round trip per group)
+    int srv[MB][NG];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int r16 = max(min(wm * WM + i * BS + 16 * g, nrows - 16), 0);   // clamped: loads stay unconditional
+        srv[i][g] = a.slot_rank[((uint32_t)row0 + (uint32_t)r16) / (uint32_t)a.BM_tile];
+      }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int rb = wm * WM + i * BS;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const int r16 = max(min(rb + 16 * g, nrows - 16), 0);   // clamped: loads stay unconditional
-        const int sr = a.slot_rank[(row0 + r16) / a.BM_tile];
+        const int sr = srv[i][g];
         const bool on = rb + 16 * g < nrows && sr >= 0;
         lg[i][g] = on ? (sr & 0xFFFF) : -1;
         rg[i][g] = on ? (sr >> 16) : 0;

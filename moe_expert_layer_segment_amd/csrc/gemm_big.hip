@@ -147,13 +147,21 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   // LoRA slot and rank of each of this wave's 16-row blocks (one align block
   // or a part of one: a single slot each), -1 / 0 without LoRA
   // (packed as slot | rank << 16, -1 without LoRA, in scalar registers)
+  // (row numbers fit in 32 bits: a 32-bit divide each, and the eight loads
+  // go out together -- with a 64-bit divide, whose branches kept each load
+  // behind the previous one's wait, the tile start took eight round trips)
   int sr[MB];
   if (lora_here) {
+    int srv[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int r16 = wm * WM + i * 16;
-      const int v = __builtin_amdgcn_readfirstlane(a.slot_rank[(row0 + min(r16, nrows - 16)) / a.BM_tile]);
-      sr[i] = r16 < nrows ? v : -1;
+      const uint32_t row = (uint32_t)row0 + (uint32_t)min(wm * WM + i * 16, nrows - 16);
+      srv[i] = a.slot_rank[row / (uint32_t)a.BM_tile];
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int v = __builtin_amdgcn_readfirstlane(srv[i]);
+      sr[i] = wm * WM + i * 16 < nrows ? v : -1;
     }
     // resolved before the first DMA: the compiler does not count the
     // inline-asm DMA, so a wait placed after it would drain the DMA too
