@@ -97,6 +97,35 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   const int64_t n0 = GATE_UP ? (int64_t)ntile * (BN / 2) : (int64_t)ntile * BN;
   auto swz = [](int row) -> int { return (row >> 1) & 7; };
 
+  // the slot words of this wave's 16-row blocks, loaded first so that they
+  // arrive with the pair ids below (one round trip).  Row numbers fit in 32
+  // bits: a 32-bit divide each (a 64-bit divide's branches kept each load
+  // behind the previous one's wait: eight round trips per tile start)
+  int srv[MB];
+  if (lora_here) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const uint32_t row = (uint32_t)row0 + (uint32_t)min(wm * WM + i * 16, nrows - 16);
+      srv[i] = a.slot_rank[row / (uint32_t)a.BM_tile];
+    }
+  }
+  // gate_up A rows are gathered: the pair id of each row this lane loads
+  int pidv[SPW];
+  if (GATE_UP && wave < A_WAVES) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int row = (wave * SPW + i) * 8 + lane / 8;
+      pidv[i] = a.sorted_ids[row0 + min(row, nrows - 1)];
+    }
+  }
+  // both groups of loads are out before either is used (left to itself the
+  // compiler moves the slot words' first use ahead of the pair-id loads)
+  if (GATE_UP && lora_here) {
+    asm volatile("" ::"v"(srv[0]), "v"(srv[1]), "v"(srv[2]), "v"(srv[3]), "v"(srv[4]), "v"(srv[5]),
+                 "v"(srv[6]), "v"(srv[7]));
+    static_assert(MB == 8, "one operand per row block");
+  }
+
   // 64-bit bases, 32-bit per-lane DMA offsets: the down A operand (act) is
   // addressed from the tile's first row; x and one expert's weights stay
   // under 4 GiB (host checks)
@@ -106,14 +135,6 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   if (wave < A_WAVES) {
     // A rows: lane l of segment s fills LDS row 8 s + l / 8, slot l % 8 with
     // global chunk (l % 8) ^ swz(row); rows past nrows load the tile's first
-    int pidv[SPW];
-    if (GATE_UP) {
-#pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int row = (wave * SPW + i) * 8 + lane / 8;
-        pidv[i] = a.sorted_ids[row0 + min(row, nrows - 1)];
-      }
-    }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int row = (wave * SPW + i) * 8 + lane / 8;
@@ -147,17 +168,8 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   // LoRA slot and rank of each of this wave's 16-row blocks (one align block
   // or a part of one: a single slot each), -1 / 0 without LoRA
   // (packed as slot | rank << 16, -1 without LoRA, in scalar registers)
-  // (row numbers fit in 32 bits: a 32-bit divide each, and the eight loads
-  // go out together -- with a 64-bit divide, whose branches kept each load
-  // behind the previous one's wait, the tile start took eight round trips)
   int sr[MB];
   if (lora_here) {
-    int srv[MB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const uint32_t row = (uint32_t)row0 + (uint32_t)min(wm * WM + i * 16, nrows - 16);
-      srv[i] = a.slot_rank[row / (uint32_t)a.BM_tile];
-    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int v = __builtin_amdgcn_readfirstlane(srv[i]);
@@ -189,6 +201,11 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // every load issued so far has been used and every store of the previous
+  // tile has been waited for by now; saying so with a wait the compiler sees
+  // keeps it from placing one after the first stage's DMA (it does not count
+  // the asm DMA, and a wait there drains it before the expand's loads go out)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   issue(0, 0);
 
   // ---- LoRA expand: acc += h[rows, q] * Bpool[l, e, q, cols], ahead of the K loop
@@ -202,8 +219,12 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   // Rank rows >= r and columns >= n_out are zero, never read.
   if (lora_here) {
     T* bt = reinterpret_cast<T*>(lds + STAGE) + wave * (64 * EXP_LD);
-    // h of this lane's row in the wave's first block, at its K offset
-    const float* hlane = a.h + (row0 + wm * WM + lrow) * a.HS + lk;
+    // operand addresses as a wave-uniform base (scalar registers) plus one
+    // 32-bit byte offset per lane: per-lane 64-bit addresses for every block
+    // were spilled and reloaded behind the first stage's DMA
+    // h: the lane's row in the wave's first block, at its K offset
+    const char* hbase = reinterpret_cast<const char*>(a.h + (row0 + wm * WM) * a.HS);
+    const uint32_t hoff = (uint32_t)((lrow * a.HS + lk) * 4);
     // blocks still to serve (wave-uniform bit mask); a pass serves every
     // block holding the slot of the lowest remaining one
     uint32_t todo = 0;
@@ -223,19 +244,20 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
         if (slot_of(i) == l) todo &= ~(1u << i);
       for (int ks = 0; ks * 32 < r; ++ks) {
         int4v braw[4];
+        const int64_t col0 = n0 + (GATE_UP ? wn * 32 : wn * 64);   // the wave's first column
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int ci = lane + 64 * t;
-          const int pi = GATE_UP ? ci >> 7 : 0;
+          const int pi = GATE_UP ? t >> 1 : 0;   // == ci >> 7: the pool is uniform per t
           const int rem = GATE_UP ? ci & 127 : ci;
           const int q = GATE_UP ? rem >> 2 : rem >> 3;
           const int cc = GATE_UP ? rem & 3 : rem & 7;
-          const int64_t col = n0 + (GATE_UP ? wn * 32 : wn * 64) + cc * 8;
           const T* pool = pi ? a.b_pool1 : a.b_pool0;
-          const int qq = ks * 32 + q;
+          const char* pbase =
+              reinterpret_cast<const char*>(pool + (((int64_t)l * a.E + e) * a.R + ks * 32) * a.n_out + col0);
           braw[t] = int4v{0, 0, 0, 0};
-          if (qq < r && col < a.n_out)
-            braw[t] = *reinterpret_cast<const int4v*>(pool + (((int64_t)l * a.E + e) * a.R + qq) * a.n_out + col);
+          if (ks * 32 + q < r && col0 + cc * 8 < a.n_out)
+            braw[t] = *reinterpret_cast<const int4v*>(pbase + (uint32_t)((q * a.n_out + cc * 8) * 2));
         }
         // transpose through the scratch: (column n, rank q) at bt[n * EXP_LD + q]
 #pragma unroll
@@ -265,11 +287,10 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
             hg[ii] = floatx8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             hu[ii] = hg[ii];
             if (slot_of(i) != l) return;
-            // a block holding a slot lies inside nrows; the block's offset from
-            // the lane's row in block 0 is a scalar
-            const int64_t boff = ((int64_t)i * 16) * a.HS + ks * 32;
-            hg[ii] = *reinterpret_cast<const floatx8*>(hlane + boff);
-            if (GATE_UP) hu[ii] = *reinterpret_cast<const floatx8*>(hlane + boff + a.RP);
+            // a block holding a slot lies inside nrows
+            const char* hb = hbase + (((int64_t)i * 16) * a.HS + ks * 32) * 4;
+            hg[ii] = *reinterpret_cast<const floatx8*>(hb + hoff);
+            if (GATE_UP) hu[ii] = *reinterpret_cast<const floatx8*>(hb + (int64_t)a.RP * 4 + hoff);
           });
           static_for<HB>([&](auto II) {
             constexpr int ii = decltype(II)::value, i = g0 + ii;
