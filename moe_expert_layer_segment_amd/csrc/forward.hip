@@ -929,6 +929,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // own, the inline-asm DMA included, so that stage then stays in flight
   // into the K loop)
   constexpr int PRE = STAGES > 2 ? STAGES - 2 : 1;
+  // every load issued so far has been used and the previous tile's stores
+  // have been waited for by now; a wait the compiler sees keeps it from
+  // placing one after these DMAs (it does not count them, and a wait there
+  // drains them before the expand's loads go out)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #pragma unroll
   for (int st = 0; st < PRE; ++st)
     if (st < nk) issue_stage(st, st);
