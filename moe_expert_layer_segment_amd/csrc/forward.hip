@@ -544,6 +544,27 @@ __device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bool pow2, b
 }
 
 
+// Tail split of the gate_up GEMM's persistent schedule.  An XCD's range of n_x
+// tiles runs on wx workgroups in q = n_x / wx full rounds and a last round of
+// r = n_x % wx tiles; when that round would leave at least 3/4 of the XCD's
+// workgroups idle for a whole tile (c4d's gate_up: 34 tiles for 32 workgroups),
+// each of its r tiles is handed out instead as S pieces of about nk / S K tiles
+// (S r <= wx, at least 2 K tiles a piece).  A piece leaves its partial sums in
+// a buffer and gate_up_fixup_kernel adds the S pieces of a tile in order and
+// finishes it (SiLU(g) * u).  S = 1: no split.
+struct TailSplit {
+  int q, r, S;
+};
+__host__ __device__ inline TailSplit tail_split(int n_x, int wx, int nk) {
+  TailSplit t{0, 0, 1};
+  if (wx <= 0 || n_x <= 0) return t;
+  t.q = n_x / wx;
+  t.r = n_x - t.q * wx;
+  if (t.r > 0 && 4 * t.r <= wx) t.S = min(wx / t.r, nk / 2);
+  if (t.S < 2) t.S = 1;
+  return t;
+}
+
 // W: weight element, T (bf16 / fp32 weights) or uint8_t (fp8 e4m3 codes with
 // 128 x 128 block scales; T = bf16).
 // GATE_UP: x rows gathered by pair, gate / up columns paired, SiLU(g) * u to act.
@@ -603,13 +624,23 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   const int xcd = blockIdx.x % 8;
   const int per_xcd = (total + 7) / 8;
   const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
+  // claims: n_main whole tiles, then (tail split) S K pieces of each tail tile
+  constexpr bool TAILS = GATE_UP && !WF8;
+  const int wx = (int)gridDim.x / 8;
+  TailSplit ts{0, 0, 1};
+  if (TAILS && a.part) ts = tail_split(t_end - t_begin, wx, (int)(a.K / BK));
+  const int n_main = ts.S > 1 ? ts.q * wx : max(t_end - t_begin, 0);
+  const int n_claims = n_main + (ts.S > 1 ? ts.r * ts.S : 0);
+  auto tile_of = [&](int j) -> int {   // logical tile of claim j, clamped to a valid index
+    const int t = t_begin + (j < n_main ? j : n_main + (j - n_main) / ts.S);
+    return max(min(t, t_end - 1), 0);
+  };
   __shared__ int claimed;
   if (threadIdx.x == 0) claimed = atomicAdd(&a.tile_ctr[xcd], 1);
   __syncthreads();
-  int logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);
-  // the record of tile `logical` (a clamped, always valid index when the loop runs)
-  int4 desc = a.tile_tab[max(min(logical, t_end - 1), 0)];
-  while (logical < t_end) {
+  int jc = __builtin_amdgcn_readfirstlane(claimed);   // this workgroup's claim
+  int4 desc = a.tile_tab[tile_of(jc)];
+  while (jc < n_claims) {
   int next_claim = 0;
   if (threadIdx.x == 0) next_claim = atomicAdd(&a.tile_ctr[xcd], 1);
   bool published = false;   // the next claim was written to LDS inside the tile
@@ -626,7 +657,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   const int split = col_t / a.n_cols;            // K split (split-major: a window shares its x rows)
   const int ntile = col_t - split * a.n_cols;
   const int64_t kper = a.K / a.ksplit;           // K elements per split, a multiple of BK
-  const bool lora_here = a.h != nullptr && split == 0;   // the expand is added once
+  // K tiles [kt0, kt0 + nk) of this tile: its split, or one piece of a tail tile
+  const int piece = jc >= n_main ? (jc - n_main) % ts.S : -1;
+  int kt_lo = 0, nk = (int)(kper / BK);
+  if (TAILS && piece >= 0) {
+    kt_lo = piece * nk / ts.S;
+    nk = (piece + 1) * nk / ts.S - kt_lo;
+  }
+  const int kt0 = split * (int)(kper / BK) + kt_lo;
+  const bool lora_here = a.h != nullptr && split == 0 && piece <= 0;   // the expand is added once
   __syncthreads();  // the previous tile's last LDS reads are done
 
   // wave index in an SGPR: every wave-level test below is a scalar branch
@@ -763,7 +802,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // this wave's DMA instructions [I0, I1) of one stage
   auto issue_part = [&](auto i0_c, auto i1_c, int stage_k, int buf) {
     constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
-    const uint32_t ktile = (uint32_t)((int64_t)split * (kper / BK) + stage_k);
+    const uint32_t ktile = (uint32_t)(kt0 + stage_k);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const int seg = wave * SEG_PER_WAVE + i;
@@ -772,7 +811,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       dma16(base, src_off[i] + ktile * (is_a ? ROWB : ROWB_B), lds_u32 + buf * STAGE_BYTES + seg * 1024);
     }
   };
-  const int nk = (int)(kper / BK);
   auto issue_stage = [&](int stage_k, int buf) {
     issue_part(std::integral_constant<int, 0>{}, std::integral_constant<int, SEG_PER_WAVE>{},
                stage_k, buf);
@@ -1174,9 +1212,25 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // the next tile's record, loaded now so that it has arrived when the
   // epilogue's stores are done (the claim was published before the K loop,
   // whose barriers made it visible)
-  next_desc = a.tile_tab[max(min(t_begin + __builtin_amdgcn_readfirstlane(claimed), t_end - 1), 0)];
+  next_desc = a.tile_tab[tile_of(__builtin_amdgcn_readfirstlane(claimed))];
   have_next = true;
 
+  // a piece of a tail tile: its partial sums go out as they sit in the
+  // registers (for each register, the wave's 64 lanes write 256 contiguous
+  // bytes); gate_up_fixup_kernel adds the pieces in order and finishes the tile
+  if constexpr (TAILS) {
+    if (piece >= 0) {
+      float* dst = a.part + (size_t)(xcd * wx + (jc - n_main)) * (BM * BN) +
+                   (size_t)wave * (MB * NB * B_::ACC * 64) + lane;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int v = 0; v < B_::ACC; ++v) dst[((i * NB + j) * B_::ACC + v) * 64] = acc[i][j][v];
+      return;
+    }
+  }
 
   // ---- epilogue -------------------------------------------------------------
   // Results go through this wave's own LDS region (the ring is idle after the
@@ -1247,10 +1301,68 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     if (threadIdx.x == 0) claimed = next_claim;
     __syncthreads();
   }
-  logical = t_begin + __builtin_amdgcn_readfirstlane(claimed);
-  if (!have_next) next_desc = a.tile_tab[max(min(logical, t_end - 1), 0)];
+  jc = __builtin_amdgcn_readfirstlane(claimed);
+  if (!have_next) next_desc = a.tile_tab[tile_of(jc)];
   desc = next_desc;
   }  // persistent tile loop
+}
+
+// Finish the tail tiles that gemm_kernel<..., GATE_UP> split into K pieces.
+// blockIdx.y = xcd * max(wx / 4, 1) + u names the u-th tail tile of that XCD
+// (wx = gemm_grid / 8, the GEMM's workgroups per XCD); each thread takes one
+// (gate, up) pair of registers of the GEMM's layout, adds its partial sums over
+// the pieces in piece order (the result does not depend on which piece ended
+// last) and writes SiLU(gate) * up to act.
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB>
+__global__ void __launch_bounds__(256) gate_up_fixup_kernel(GemmArgs<T> a, int gemm_grid) {
+  typedef Elt<T> E_;
+  typedef Blk<T> B_;
+  constexpr int BS = B_::BS, ACC = B_::ACC;
+  constexpr int BK = ROWB / sizeof(T);
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int MB = WM / BS, NB = WN / BS;
+  const int wx = gemm_grid / 8;
+  const int maxr = max(wx / 4, 1);
+  const int xcd = blockIdx.y / maxr, u = blockIdx.y % maxr;
+  const int t = blockIdx.x * 256 + threadIdx.x;   // register pair of the tile
+  if (xcd >= 8 || !a.part || t >= BM * BN / 2) return;
+  const int count = min(a.item_count[0], a.max_items);
+  const int total = count * a.n_tiles;
+  const int per_xcd = (total + 7) / 8;
+  const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
+  const TailSplit ts = tail_split(t_end - t_begin, wx, (int)(a.K / BK));
+  if (ts.S < 2 || u >= ts.r) return;
+  const int4 desc = a.tile_tab[t_begin + ts.q * wx + u];
+  const int col_t = desc.w;
+  const int64_t row0 = desc.x;
+  const int nrows = desc.y;
+  const int e = desc.z;
+  // the GEMM skipped such records (no pieces were written)
+  if (col_t < 0 || col_t >= a.n_tiles || row0 < 0 || nrows <= 0 || nrows > BM || (nrows & 15) ||
+      (row0 & 15) || row0 + nrows > a.cap || e < 0 || e >= a.E)
+    return;
+  // t = (((wave * MB + i) * NB/2 + j) * ACC + v) * 64 + lane, j < NB/2 (gate);
+  // its up partner is column block j + NB/2
+  const int lane = t % 64;
+  int rest = t / 64;
+  const int v = rest % ACC;
+  rest /= ACC;
+  const int j = rest % (NB / 2);
+  rest /= NB / 2;
+  const int i = rest % MB, wave = rest / MB;
+  const size_t og = ((((size_t)wave * MB + i) * NB + j) * ACC + v) * 64 + lane;
+  const size_t ou = og + (size_t)(NB / 2) * ACC * 64;
+  const float* src = a.part + (size_t)(xcd * wx + u * ts.S) * (BM * BN);
+  float g = 0.0f, up = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < ts.S; ++s) {
+    g += src[(size_t)s * (BM * BN) + og];
+    up += src[(size_t)s * (BM * BN) + ou];
+  }
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int r = wm * WM + i * BS + B_::row(v, lane);
+  const int64_t col = (int64_t)col_t * (BN / 2) + wn * (WN / 2) + j * BS + lane % BS;
+  if (r < nrows && col < a.n_out) a.act[(row0 + r) * a.n_out + col] = E_::from_float(silu_f(g) * up);
 }
 
 // --------------------------------------------------------------------------
@@ -1503,6 +1615,18 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
   w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
+  // the general gate_up GEMM with bf16 / fp32 weights may split tail tiles
+  // into K pieces (one partial tile per workgroup of its grid) when its tiles
+  // are long: with fewer than 64 K tiles a split saves less than the extra
+  // launch that finishes the pieces costs (measured on the decode batches)
+  const int64_t bk_gu = p.dtype == 1 ? TileCfg<bf16_t>::ROWB / 2 : TileCfg<float>::ROWB / 4;
+  if (!w.big && p.wdtype != kWeightFp8 && p.H >= 64 * bk_gu) {
+    const int per_cu = p.dtype == 1 ? TileCfg<bf16_t>::PER_CU : TileCfg<float>::PER_CU;
+    const int64_t tile_elems = p.dtype == 1 ? (int64_t)TileCfg<bf16_t>::BM * TileCfg<bf16_t>::BN
+                                            : (int64_t)TileCfg<float>::BM * TileCfg<float>::BN;
+    w.grid_gu = gemm_grid(w.n_tiles_gu * w.max_items, per_cu);
+    w.part_off = take(sizeof(float) * (size_t)(w.grid_gu * tile_elems));
+  }
   w.bytes = off;
   return w;
 }
@@ -1628,9 +1752,19 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
                            dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
       }
     }
-    if (!fp8w && !w.big)
-      launch_timed((gemm_kernel<T, T, TileCfg<T>::BM, BN, TileCfg<T>::WM, TileCfg<T>::WN, TileCfg<T>::STAGES, TileCfg<T>::ROWB, true>),
-                            dim3((unsigned)nblk), dim3(64 * TileCfg<T>::WM * TileCfg<T>::WN), stream, ev0, ev1, a);
+    if (!fp8w && !w.big) {
+      typedef TileCfg<T> C;
+      const bool tails = w.grid_gu > 0;
+      if (tails && nblk != w.grid_gu) return hipErrorInvalidValue;   // the partial buffer is sized for this grid
+      a.part = tails ? reinterpret_cast<float*>(ws + w.part_off) : nullptr;
+      launch_timed((gemm_kernel<T, T, C::BM, BN, C::WM, C::WN, C::STAGES, C::ROWB, true>),
+                   dim3((unsigned)nblk), dim3(64 * C::WM * C::WN), stream, ev0, tails ? nullptr : ev1, a);
+      // tail tiles split into K pieces (if any): add the pieces, SiLU(g) * u
+      if (tails)
+        launch_timed((gate_up_fixup_kernel<T, C::BM, BN, C::WM, C::WN, C::ROWB>),
+                     dim3((unsigned)ceil_div(C::BM * BN / 2, 256), (unsigned)(8 * std::max<int64_t>(nblk / 8 / 4, 1))),
+                     dim3(256), stream, nullptr, ev1, a, (int)nblk);
+    }
   }
   mark(2 * kStageShrinkA);
   if (lora && groups > 0) {

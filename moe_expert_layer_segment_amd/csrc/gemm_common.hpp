@@ -41,6 +41,8 @@ struct GemmArgs {
   const int32_t* slot_rank;   // [cap / BM_tile] slot | rank << 16 per align block, or -1
   int64_t n_split;            // dense mode: output columns [0, n_split) use b_pool0 and h[:, :RP],
                               // the rest b_pool1 and h[:, RP:2RP] (a multiple of 32)
+  float* part;                // gate_up: partial sums of tail-tile K pieces, [gridDim.x][BM * BN]
+                              // (null: no tail split)
 };
 
 

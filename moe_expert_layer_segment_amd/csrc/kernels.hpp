@@ -70,7 +70,8 @@ struct ForwardWs {
   int64_t cap, max_items, RP;
   int64_t n_tiles_gu = 0, n_tiles_dn = 0;   // column tiles (x K splits) of the two GEMMs
   size_t items_off, count_off, tab_gu_off, tab_dn_off, slot_rank_off, hgu_off, act_off, hd_off, z_off,
-      bytes;
+      part_off = 0, bytes;
+  int64_t grid_gu = 0;             // workgroups of the general gate_up GEMM (0: tail split unused)
   int split_gu = 1, split_d = 1;   // K splits of the two shrinks
   bool shrink4 = false;            // shrinks share pool rows across 4 row groups
   int split_down_k = 1;            // K splits of the down GEMM (planes of z)

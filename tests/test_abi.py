@@ -188,8 +188,10 @@ def test_forward_fp8_weight_validation():
     assert call(struct_size=old, weight_dtype=3) == binding.ERR_WORKSPACE
     assert call(struct_size=old + 4, weight_dtype=3) == binding.ERR_WORKSPACE   # with its padding
     assert call(struct_size=old - 4) == binding.ERR_INVALID
+    # fp8 weights need no buffer beyond the bf16 layout (which also holds the
+    # partial sums of split gate_up tail tiles, unused with fp8 weights)
     ws8 = lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs(weight_dtype=F8)))
-    assert ws8 == lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
+    assert 0 < ws8 <= lib.moe_lora_forward_workspace_bytes(ctypes.byref(_fargs()))
 
 
 def _dargs(**over):
