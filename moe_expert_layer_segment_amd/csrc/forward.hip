@@ -1509,10 +1509,10 @@ static int down_ksplit_big(int64_t P, int64_t E, int64_t H, int64_t I) {
 // K splits of a shrink: enough workgroups to fill the GPU when the batch has
 // few rows (decode), each split at least 512 deep and a multiple of 128 (the
 // four waves' interleaved 32-deep steps).
-// The shrink shares pool rows across 4 row groups on large batches whose
-// (expert, slot) buckets hold at least 64 pairs on average (4 groups of 16
-// rows).  Smaller buckets leave little to share; on smaller batches the
-// narrower grid and its per-chunk barriers cost more than the pool re-reads.
+// The shrink shares pool rows across the row groups of a workgroup on large
+// batches whose (expert, slot) buckets hold at least 64 pairs on average.
+// Smaller buckets leave little to share; on smaller batches the narrower grid
+// and its per-chunk barriers cost more than the pool re-reads.
 #ifndef MOELORA_SHRINK4_MIN_ROWS
 #define MOELORA_SHRINK4_MIN_ROWS 64
 #endif
@@ -1520,9 +1520,12 @@ static int down_ksplit_big(int64_t P, int64_t E, int64_t H, int64_t I) {
 #define MOELORA_SHRINK4_MIN_P 65536
 #endif
 
-// waves (16-row groups) per workgroup of the LDS-shared shrink
+// waves (16-row groups) per workgroup of the LDS-shared shrink: 8 halves the
+// pool-row traffic of 4 (each 256-byte pool chunk serves 128 rows), and with
+// the deeper K split below took c4p's gate_up shrink from 0.86 to 0.65 ms
+// (down shrink 0.19 -> 0.18; 16 waves: 0.78 ms)
 #ifndef MOELORA_SHRINK_SHARED_WAVES
-#define MOELORA_SHRINK_SHARED_WAVES 4
+#define MOELORA_SHRINK_SHARED_WAVES 8
 #endif
 static constexpr int kShrinkSharedWaves = MOELORA_SHRINK_SHARED_WAVES;
 
@@ -1550,13 +1553,20 @@ static void launch_shrink(const ShrinkArgs<T>& s, int64_t groups, int splits, bo
 #ifndef MOELORA_SHRINK_WGS
 #define MOELORA_SHRINK_WGS 1024
 #endif
+// the LDS-shared shrink's own target: K splits until about this many
+// workgroups (c4p gate_up: 4 splits of 1792; 1024 (one split) 0.86 ms with 4
+// waves, 2048 0.70, 4096 0.65)
+#ifndef MOELORA_SHRINK4_WGS
+#define MOELORA_SHRINK4_WGS 4096
+#endif
 #ifndef MOELORA_SHRINK_MIN_K
 #define MOELORA_SHRINK_MIN_K 512
 #endif
 static int64_t shrink_kchunk(int64_t P, int64_t K, bool shared, int npool) {
   const int64_t groups = P / 16 + 1;
   const int64_t wgs = shared ? ceil_div(groups, kShrinkSharedWaves) : groups;
-  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(MOELORA_SHRINK_WGS, wgs)));
+  const int64_t target = shared ? MOELORA_SHRINK4_WGS : MOELORA_SHRINK_WGS;
+  int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(target, wgs)));
   s = std::min<int64_t>(s, std::max<int64_t>(1, K / ((int64_t)npool * MOELORA_SHRINK_MIN_K)));
   return round_up(ceil_div(K, s), 128);
 }
