@@ -61,6 +61,8 @@ def parse():
 
 # kernel name (rocprofv3, mangled or not) -> forward stage or metadata kernel
 def _stage_of(kname):
+    if "gate_up_fixup_kernel" in kname:   # finishes the gate_up tail tiles split into K pieces
+        return "gate_up_fixup"
     if "gemm_kernel" in kname or "gemm_big_kernel" in kname:
         gate_up = ("Lb1E" in kname) or kname.rstrip(") ").split("(")[0].endswith("true>")
         return "gate_up_gemm" if gate_up else "down_gemm"
