@@ -19,7 +19,11 @@
 
 namespace moelora {
 
-static constexpr int kAlignSteps = 8;       // at most this many 64-pair steps per wave in the count kernel
+// at most this many 64-pair steps per wave in the count kernel: fewer, longer
+// chunks shorten the one-workgroup scan (chunks x keys) more than they lengthen
+// the count (align on c4p 95 -> 67 us, c2 58 -> 48 us against 8 steps; 32 steps
+// lose on c2 and c3)
+static constexpr int kAlignSteps = 16;
 static constexpr int kScanThreads = 1024;
 static constexpr int kScatterThreads = 256;
 
