@@ -547,7 +547,8 @@ __device__ __forceinline__ void fp8x16_to_bf16(int4v raw, float sc, bool pow2, b
 // Tail split of the gate_up GEMM's persistent schedule.  An XCD's range of n_x
 // tiles runs on wx workgroups in q = n_x / wx full rounds and a last round of
 // r = n_x % wx tiles; when that round would leave at least 3/4 of the XCD's
-// workgroups idle for a whole tile (c4d's gate_up: 34 tiles for 32 workgroups),
+// workgroups idle for a whole tile (the 128-token decode batch
+// over 256 experts of H = 7168: 34 tiles for 32 workgroups),
 // each of its r tiles is handed out instead as S pieces of about nk / S K tiles
 // (S r <= wx, at least 2 K tiles a piece).  A piece leaves its partial sums in
 // a buffer and gate_up_fixup_kernel adds the S pieces of a tile in order and
@@ -625,7 +626,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   const int per_xcd = (total + 7) / 8;
   const int t_begin = xcd * per_xcd, t_end = min(total, t_begin + per_xcd);
   // claims: n_main whole tiles, then (tail split) S K pieces of each tail tile
-  constexpr bool TAILS = GATE_UP && !WF8;
+  constexpr bool TAILS = GATE_UP;
   const int wx = (int)gridDim.x / 8;
   TailSplit ts{0, 0, 1};
   if (TAILS && a.part) ts = tail_split(t_end - t_begin, wx, (int)(a.K / BK));
@@ -835,8 +836,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
     if (GATE_UP) return n0 + wn * (WN / 2) + (j % (NB / 2)) * BS;
     return n0 + wn * WN + j * BS;
   };
-  // fp8 weights: this wave's block scales of the tile's K range into sc_lds
-  // (the wave reads only its own entries, so no barrier is needed)
+  // fp8 weights: this wave's block scales of the K split's range into sc_lds
+  // (the wave reads only its own entries, so no barrier is needed); a piece
+  // of a tail tile reads them from its first K tile kt_lo on
   auto fill_scales = [&]() {
     const int nkb = (int)(kper / 128);
     const int64_t kbs = a.K / 128, rows128 = a.w_rows / 128;
@@ -929,7 +931,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
         for (int j = 0; j < NB; ++j) {
           // one scale per wave (its columns share a 128-row block): a scalar
           const uint32_t bits = __builtin_amdgcn_readfirstlane(
-              __builtin_bit_cast(uint32_t, sc_lds[(wave * NB + j) * MAXKB + (kt * BK) / 128]));
+              __builtin_bit_cast(uint32_t, sc_lds[(wave * NB + j) * MAXKB + ((kt_lo + kt) * BK) / 128]));
           sck[j] = __builtin_bit_cast(float, bits);
           const uint32_t ex = (bits >> 23) & 0xFF;
           sc_pow2[j] = (bits & 0x807FFFFFu) == 0 && ex != 0 && ex != 0xFF;
@@ -1444,8 +1446,14 @@ struct Fp8DecodeCfg {
 #endif
 static_assert(Fp8Cfg::BM == TileCfg<bf16_t>::BM && Fp8Cfg::BN == TileCfg<bf16_t>::BN &&
                   Fp8Cfg::BN == TileCfg<bf16_t>::BN_DOWN && Fp8DecodeCfg::BM == Fp8Cfg::BM &&
-                  Fp8DecodeCfg::BN == Fp8Cfg::BN,
-              "fp8 tiles share the work items and column tiles of the bf16 path");
+                  Fp8DecodeCfg::BN == Fp8Cfg::BN && Fp8Cfg::PER_CU == TileCfg<bf16_t>::PER_CU &&
+                  Fp8DecodeCfg::PER_CU == Fp8Cfg::PER_CU,
+              "fp8 tiles share the work items, column tiles, grid and partial tiles of the bf16 path");
+// fp8 weights take 128-deep K tiles when a batch routes at least
+// MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT pairs per expert, else 64-deep ones
+static bool fp8_deep_k_tiles(int64_t P, int64_t E) {
+  return P >= (int64_t)MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT * E;
+}
 template <> struct TileCfg<float> {
   static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, STAGES = 3, ROWB = 128, PER_CU = 2;
   static constexpr int BN_DOWN = 64, STAGES_DOWN = 3;
@@ -1587,6 +1595,20 @@ static void launch_timed(void (*kernel)(Args...), dim3 grid, dim3 block, hipStre
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
 }
 
+// The general gate_up GEMM, then, when it splits tail tiles into K pieces
+// (a.part set), the kernel that adds the pieces and finishes those tiles.
+template <typename T, typename W, typename F>
+static void launch_gate_up(const GemmArgs<T>& a, int64_t nblk, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+  const bool tails = a.part != nullptr;
+  launch_timed((gemm_kernel<T, W, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
+               dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, tails ? nullptr : ev1, a);
+  if (tails)
+    launch_timed((gate_up_fixup_kernel<T, F::BM, F::BN, F::WM, F::WN, F::ROWB>),
+                 dim3((unsigned)ceil_div(F::BM * F::BN / 2, 256), (unsigned)(8 * std::max<int64_t>(nblk / 8 / 4, 1))),
+                 dim3(256), stream, nullptr, ev1, a, (int)nblk);
+}
+
 ForwardWs forward_ws_layout(const ForwardProblem& p) {
   ForwardWs w;
   const int64_t P = p.T * p.k;
@@ -1625,12 +1647,14 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
   w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
-  // the general gate_up GEMM with bf16 / fp32 weights may split tail tiles
-  // into K pieces (one partial tile per workgroup of its grid) when its tiles
-  // are long: with fewer than 64 K tiles a split saves less than the extra
-  // launch that finishes the pieces costs (measured on the decode batches)
-  const int64_t bk_gu = p.dtype == 1 ? TileCfg<bf16_t>::ROWB / 2 : TileCfg<float>::ROWB / 4;
-  if (!w.big && p.wdtype != kWeightFp8 && p.H >= 64 * bk_gu) {
+  // the general gate_up GEMM may split tail tiles into K pieces (one partial
+  // tile per workgroup of its grid) when its tiles are long: with fewer than
+  // 64 K tiles a split saves less than the extra launch that finishes the
+  // pieces costs (measured on the decode batches)
+  const bool fp8w = p.dtype == 1 && p.wdtype == kWeightFp8;
+  const int64_t bk_gu = !fp8w ? (p.dtype == 1 ? TileCfg<bf16_t>::ROWB / 2 : TileCfg<float>::ROWB / 4)
+                        : fp8_deep_k_tiles(P, p.E) ? Fp8Cfg::ROWB / 2 : Fp8DecodeCfg::ROWB / 2;
+  if (!w.big && p.H >= 64 * bk_gu) {
     const int per_cu = p.dtype == 1 ? TileCfg<bf16_t>::PER_CU : TileCfg<float>::PER_CU;
     const int64_t tile_elems = p.dtype == 1 ? (int64_t)TileCfg<bf16_t>::BM * TileCfg<bf16_t>::BN
                                             : (int64_t)TileCfg<float>::BM * TileCfg<float>::BN;
@@ -1664,7 +1688,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   constexpr int BN = TileCfg<T>::BN;
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   const bool fp8w = kBf16 && p.wdtype == kWeightFp8;
-  const bool fp8_deep_k = P >= (int64_t)MOELORA_FP8_DEEP_K_MIN_PAIRS_PER_EXPERT * p.E;
+  const bool fp8_deep_k = fp8_deep_k_tiles(P, p.E);
 
   mark(2 * kStagePlan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, (int)p.E, (int)p.BM, BM,
@@ -1749,32 +1773,19 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     a.tile_ctr = count + 4;
     int64_t nblk = gemm_grid((int64_t)a.n_tiles * w.max_items, TileCfg<T>::PER_CU);
     hipEvent_t ev0 = events ? events[2 * kStageGateUp] : nullptr, ev1 = events ? events[2 * kStageGateUp + 1] : nullptr;
+    if (w.grid_gu > 0) {
+      if (nblk != w.grid_gu) return hipErrorInvalidValue;   // the partial buffer is sized for this grid
+      a.part = reinterpret_cast<float*>(ws + w.part_off);
+    }
     if constexpr (kBf16) {
-      if (w.big) {
+      if (w.big)
         launch_gemm_big(true, a, nblk, stream, ev0, ev1);
-      } else if (fp8w && fp8_deep_k) {
-        typedef Fp8Cfg F;
-        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
-      } else if (fp8w) {
-        typedef Fp8DecodeCfg F;
-        launch_timed((gemm_kernel<T, uint8_t, F::BM, F::BN, F::WM, F::WN, F::STAGES, F::ROWB, true>),
-                           dim3((unsigned)nblk), dim3(64 * F::WM * F::WN), stream, ev0, ev1, a);
-      }
+      else if (fp8w && fp8_deep_k)
+        launch_gate_up<T, uint8_t, Fp8Cfg>(a, nblk, stream, ev0, ev1);
+      else if (fp8w)
+        launch_gate_up<T, uint8_t, Fp8DecodeCfg>(a, nblk, stream, ev0, ev1);
     }
-    if (!fp8w && !w.big) {
-      typedef TileCfg<T> C;
-      const bool tails = w.grid_gu > 0;
-      if (tails && nblk != w.grid_gu) return hipErrorInvalidValue;   // the partial buffer is sized for this grid
-      a.part = tails ? reinterpret_cast<float*>(ws + w.part_off) : nullptr;
-      launch_timed((gemm_kernel<T, T, C::BM, BN, C::WM, C::WN, C::STAGES, C::ROWB, true>),
-                   dim3((unsigned)nblk), dim3(64 * C::WM * C::WN), stream, ev0, tails ? nullptr : ev1, a);
-      // tail tiles split into K pieces (if any): add the pieces, SiLU(g) * u
-      if (tails)
-        launch_timed((gate_up_fixup_kernel<T, C::BM, BN, C::WM, C::WN, C::ROWB>),
-                     dim3((unsigned)ceil_div(C::BM * BN / 2, 256), (unsigned)(8 * std::max<int64_t>(nblk / 8 / 4, 1))),
-                     dim3(256), stream, nullptr, ev1, a, (int)nblk);
-    }
+    if (!fp8w && !w.big) launch_gate_up<T, T, TileCfg<T>>(a, nblk, stream, ev0, ev1);
   }
   mark(2 * kStageShrinkA);
   if (lora && groups > 0) {

@@ -113,3 +113,41 @@ def run(inp, block_m=16, with_lora=True, out_dtype=None):
     y = binding.run_layer(inp, block_m=block_m, with_lora=with_lora, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return y
+
+
+def gate_up_tail_split(spec, block_m=16):
+    """Which XCD ranges of the general gate_up GEMM split their tail tiles into
+    K pieces, recomputed from the library's rule: the host's grid (from its
+    bound on work items), the device's item count (from the oracle's align),
+    per-XCD tile ranges of ceil(tiles / 8), and for a range of n_x tiles on
+    wx = grid / 8 workgroups a tail r = n_x % wx with 0 < 4 r <= wx split into
+    S = min(wx / r, K tiles / 2) pieces (S >= 2; only when K has >= 64 K tiles).
+    Returns (xcd, full rounds, tail tiles, pieces) of each splitting range."""
+    bf = spec.dtype == "bf16"
+    rpi, BN, per_cu, BK = (128, 256, 1, 64) if bf else (64, 64, 2, 32)
+    T = int(sum(spec.seg_lens))
+    P = T * spec.top_k
+    if spec.weights.startswith("fp8"):   # 128-deep K tiles from 64 pairs per expert on
+        BK = 128 if P >= 64 * spec.num_experts else 64
+    ids, _ = workloads.route(workloads.router_logits(spec), spec.top_k)
+    seg = np.concatenate([[0], np.cumsum(spec.seg_lens)]).astype(np.int32)
+    en, mp = oracle.moe_lora_info(T, seg, np.array(spec.weight_indices, np.int32),
+                                  np.array(spec.lora_ranks, np.int32), max(spec.seg_lens))
+    al = oracle.moe_lora_align(ids.astype(np.int32), mp, en, spec.num_experts, spec.num_loras, block_m)
+    cap = oracle.align_capacity_rows(P, spec.num_experts, spec.num_loras, block_m)
+    max_items = -(-cap // rpi) + min(P, spec.num_experts)
+    n_tiles = -(-spec.inter // (BN // 2))
+    grid = min(256 * per_cu, -(-n_tiles * max_items // 8) * 8)
+    eto = al["expert_tile_offsets"]
+    count = min(max_items, sum(-(-int(eto[e + 1] - eto[e]) * block_m // rpi) for e in range(spec.num_experts)))
+    total, wx, nk = count * n_tiles, grid // 8, spec.hidden // BK
+    if nk < 64:
+        return []
+    per = -(-total // 8)
+    out = []
+    for x in range(8):
+        n_x = max(0, min(total, (x + 1) * per) - x * per)
+        q, r = divmod(n_x, wx)
+        if 0 < r and 4 * r <= wx and min(wx // r, nk // 2) >= 2:
+            out.append((x, q, r, min(wx // r, nk // 2)))
+    return out

@@ -17,7 +17,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (POOLS, assert_layer_close, gpu_inputs, oracle_forward, run, say, to_np)
+from gpu_helpers import (POOLS, assert_layer_close, gate_up_tail_split, gpu_inputs, oracle_forward, run,
+                         say, to_np)
 from moe_expert_layer_segment_amd import binding, workloads
 
 pytestmark = pytest.mark.gpu
@@ -129,41 +130,6 @@ def test_small_full(case):
     _check(got, ref, dt, name)
 
 
-def _gate_up_tail_split(spec, block_m=16):
-    """Which XCD ranges of the general gate_up GEMM split their tail tiles into
-    K pieces, recomputed from the library's rule: the host's grid (from its
-    bound on work items), the device's item count (from the oracle's align),
-    per-XCD tile ranges of ceil(tiles / 8), and for a range of n_x tiles on
-    wx = grid / 8 workgroups a tail r = n_x % wx with 0 < 4 r <= wx split into
-    S = min(wx / r, K tiles / 2) pieces (S >= 2; only when K has >= 64 K tiles)."""
-    bf = spec.dtype == "bf16"
-    rpi, BN, per_cu, BK = (128, 256, 1, 64) if bf else (64, 64, 2, 32)
-    T = int(sum(spec.seg_lens))
-    P = T * spec.top_k
-    ids, _ = workloads.route(workloads.router_logits(spec), spec.top_k)
-    seg = np.concatenate([[0], np.cumsum(spec.seg_lens)]).astype(np.int32)
-    en, mp = oracle.moe_lora_info(T, seg, np.array(spec.weight_indices, np.int32),
-                                  np.array(spec.lora_ranks, np.int32), max(spec.seg_lens))
-    al = oracle.moe_lora_align(ids.astype(np.int32), mp, en, spec.num_experts, spec.num_loras, block_m)
-    cap = oracle.align_capacity_rows(P, spec.num_experts, spec.num_loras, block_m)
-    max_items = -(-cap // rpi) + min(P, spec.num_experts)
-    n_tiles = -(-spec.inter // (BN // 2))
-    grid = min(256 * per_cu, -(-n_tiles * max_items // 8) * 8)
-    eto = al["expert_tile_offsets"]
-    count = min(max_items, sum(-(-int(eto[e + 1] - eto[e]) * block_m // rpi) for e in range(spec.num_experts)))
-    total, wx, nk = count * n_tiles, grid // 8, spec.hidden // BK
-    if nk < 64:
-        return []
-    per = -(-total // 8)
-    out = []
-    for x in range(8):
-        n_x = max(0, min(total, (x + 1) * per) - x * per)
-        q, r = divmod(n_x, wx)
-        if 0 < r and 4 * r <= wx and min(wx // r, nk // 2) >= 2:
-            out.append((x, q, r, min(wx // r, nk // 2)))
-    return out
-
-
 @pytest.mark.parametrize("dt,H,I", [("bf16", 4096, 256), ("f32", 2048, 128)])
 def test_gate_up_tail_split(dt, H, I):
     """Few work items for a grid sized by the host's bound: the gate_up GEMM
@@ -171,7 +137,7 @@ def test_gate_up_tail_split(dt, H, I):
     expand in the first piece only).  Every token against the oracle."""
     spec = workloads.LayerSpec("tail_split_" + dt, 64, 2, H, I, 3, [16, 0, 32], [20, 30, 14], [0, 2, -1],
                                dtype=dt, seed=2, pool_rank=32, router="uniform_bias")
-    split = _gate_up_tail_split(spec)
+    split = gate_up_tail_split(spec)
     say(f"forward tail split {dt}: (xcd, full rounds, tail tiles, pieces) {split}")
     assert split, "the shape no longer exercises the tail split"
     inp = gpu_inputs(spec)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_layer_close, gpu_inputs, oracle_forward, run, say, to_np
+from gpu_helpers import assert_layer_close, gate_up_tail_split, gpu_inputs, oracle_forward, run, say, to_np
 from moe_expert_layer_segment_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -65,6 +65,22 @@ def test_fp8_down_k_split(E, lens):
     say(f"forward fp8 with the down GEMM's K split (I = 8192, E = {E})")
     inp = gpu_inputs(spec)
     assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", "fp8 down K split")
+
+
+@pytest.mark.parametrize("scales", ["fp8", "fp8_f32scale"])
+@pytest.mark.parametrize("E,H,I,lens", [(64, 4096, 256, [20, 30, 14]), (4, 8192, 768, [100, 100, 100])],
+                         ids=["decode_tiles", "deep_k_tiles"])
+def test_fp8_gate_up_tail_split(E, H, I, lens, scales):
+    """Few work items for the grid: the fp8 gate_up GEMM hands its last tiles out
+    as K pieces, each taking the block scales from its own first K tile, and a
+    second kernel adds them.  Every token against the oracle."""
+    spec = workloads.LayerSpec("fp8_tail_split", E, 2, H, I, 3, [16, 0, 32], lens, [0, 2, -1], seed=2,
+                               pool_rank=32, router="uniform_bias", weights=scales)
+    split = gate_up_tail_split(spec)
+    say(f"forward fp8 tail split E={E} H={H} ({scales}): (xcd, full rounds, tail tiles, pieces) {split}")
+    assert split, "the shape no longer exercises the tail split"
+    inp = gpu_inputs(spec)
+    assert_layer_close(_y32(inp), oracle_forward(inp), "bf16", f"fp8 tail split E={E} {scales}")
 
 
 @pytest.mark.parametrize("name,n_sample", [("c1_fp8", 40), ("c4p_fp8", 12), ("c3_fp8", 0),
