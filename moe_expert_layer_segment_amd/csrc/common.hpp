@@ -15,6 +15,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -69,6 +70,33 @@ __device__ inline typename Elt<T>::frag load_frag_global(const T* p) {
 // SiLU(v) = v * sigmoid(v) = v / (1 + e^-v), with e^-v evaluated as
 // 2^(-v * log2(e)) on the hardware exp2 unit and the division as a multiply
 // by the hardware reciprocal (about 1 ulp; for e^-v = inf it gives 0).
+// The weighted down rows (z) of a bf16 layer, stored for the combine: each
+// fp32 value rounded to its top 24 bits (sign, exponent and 15 explicit
+// significand bits, round to nearest even: a relative error of at most 2^-16),
+// four values packed into three 32-bit words.  Infinities and NaNs are cut,
+// not rounded, so they stay what they are.
+__device__ inline uint32_t fp24_bits(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t r = (u & 0x7F800000u) == 0x7F800000u ? u : u + 0x7Fu + ((u >> 8) & 1u);
+  return r >> 8;
+}
+__device__ inline u32x3 fp24_pack4(floatx4 v) {
+  const uint32_t a = fp24_bits(v[0]), b = fp24_bits(v[1]), c = fp24_bits(v[2]), d = fp24_bits(v[3]);
+  u32x3 w;
+  w[0] = a | (b << 24);
+  w[1] = (b >> 8) | (c << 16);
+  w[2] = (c >> 16) | (d << 8);
+  return w;
+}
+__device__ inline floatx4 fp24_unpack4(u32x3 w) {
+  floatx4 v;
+  v[0] = __builtin_bit_cast(float, w[0] << 8);
+  v[1] = __builtin_bit_cast(float, (w[1] << 16) | ((w[0] >> 16) & 0xFF00u));
+  v[2] = __builtin_bit_cast(float, (w[2] << 24) | ((w[1] >> 8) & 0xFFFF00u));
+  v[3] = __builtin_bit_cast(float, w[2] & 0xFFFFFF00u);
+  return v;
+}
+
 __device__ inline float silu_f(float v) {
   const float kLog2e = 1.4426950408889634f;
   float e = __builtin_amdgcn_exp2f(-v * kLog2e);

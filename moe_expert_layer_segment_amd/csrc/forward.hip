@@ -1238,7 +1238,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
   // Results go through this wave's own LDS region (the ring is idle after the
   // barrier that ended the K loop) so that every lane stores 16 contiguous
   // bytes: a lane's accumulators hold one column of several rows.
-  constexpr int CH = 16 / (GATE_UP ? (int)sizeof(T) : 4);   // elements per 16-byte chunk
+  constexpr int CH = 16 / (GATE_UP ? (int)sizeof(T) : 4);   // elements per 16-byte chunk (of fp32 for z)
+  // z of a bf16 layer in 24-bit form (fp24_pack4); fp32 layers and the dense
+  // projection (whose z is its output) keep fp32
+  constexpr bool Z24 = sizeof(T) == 2 && !DENSE;
   if (GATE_UP) {
     // act = SiLU(gate) * up, [WM rows][WN/2 cols] of T per wave
     constexpr int EW = WN / 2;
@@ -1294,7 +1297,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       floatx4 vv = *reinterpret_cast<const floatx4*>(ep + r * WN + cc * CH);
 #pragma unroll
       for (int q = 0; q < 4; ++q) vv[q] = wgt * vv[q];
-      *reinterpret_cast<floatx4*>(a.z + ((int64_t)split * a.P + pid) * a.n_out + col) = vv;
+      const int64_t zi = ((int64_t)split * a.P + pid) * a.n_out + col;
+      if constexpr (Z24)   // 4 values in 12 bytes
+        *reinterpret_cast<u32x3*>(static_cast<char*>(a.z) + zi * 3) = fp24_pack4(vv);
+      else
+        *reinterpret_cast<floatx4*>(static_cast<float*>(a.z) + zi) = vv;
     }
   }
   }();
@@ -1369,11 +1376,12 @@ __global__ void __launch_bounds__(256) gate_up_fixup_kernel(GemmArgs<T> a, int g
 
 // --------------------------------------------------------------------------
 // combine: y[t, c] = sum_j sum_q z[q, t*k + j, c]  (j, then the down GEMM's
-// K splits q, in order, fp32)
+// K splits q, in order, fp32).  z in fp32, or (Z24) in the 24-bit form of a
+// bf16 layer, 4 columns in 12 bytes; a thread takes 4 columns.
 // --------------------------------------------------------------------------
-template <typename ZT, typename OutT>
+template <bool Z24, typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const ZT* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H,
+combine_kernel(const void* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k, int64_t H,
                int nsplit, int64_t split_stride) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T_ * H) return;
@@ -1381,15 +1389,11 @@ combine_kernel(const ZT* __restrict__ z, OutT* __restrict__ y, int64_t T_, int k
   floatx4 s = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j)
     for (int q = 0; q < nsplit; ++q) {   // pair j's K splits, in order
-      const ZT* zp = z + q * split_stride + (t * k + j) * H + c;
-      if constexpr (sizeof(ZT) == 4) {
-        s += *reinterpret_cast<const floatx4*>(zp);
-      } else {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 v = *reinterpret_cast<const bf16x4*>(zp);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s[u] += (float)v[u];
-      }
+      const int64_t zi = q * split_stride + (t * k + j) * H + c;
+      if constexpr (Z24)
+        s += fp24_unpack4(*reinterpret_cast<const u32x3*>(static_cast<const char*>(z) + zi * 3));
+      else
+        s += *reinterpret_cast<const floatx4*>(static_cast<const float*>(z) + zi);
     }
 #pragma unroll
   for (int q = 0; q < 4; ++q) y[i + q] = Elt<OutT>::from_float(s[q]);
@@ -1646,7 +1650,7 @@ ForwardWs forward_ws_layout(const ForwardProblem& p) {
   w.hgu_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_gu * w.cap * 2 * w.RP : 0);
   w.act_off = take(esz * (size_t)w.cap * p.I);
   w.hd_off = take(p.L > 0 ? sizeof(float) * (size_t)w.split_d * w.cap * w.RP : 0);
-  w.z_off = take(sizeof(float) * (size_t)w.split_down_k * P * p.H);
+  w.z_off = take((p.dtype == 1 ? 3 : 4) * (size_t)w.split_down_k * P * p.H);   // 24-bit z for bf16 layers
   // the general gate_up GEMM may split tail tiles into K pieces (one partial
   // tile per workgroup of its grid) when its tiles are long: with fewer than
   // 64 K tiles a split saves less than the extra launch that finishes the
@@ -1681,7 +1685,7 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
   float* hgu = reinterpret_cast<float*>(ws + w.hgu_off);
   T* act = reinterpret_cast<T*>(ws + w.act_off);
   float* hd = reinterpret_cast<float*>(ws + w.hd_off);
-  float* z = reinterpret_cast<float*>(ws + w.z_off);
+  void* z = ws + w.z_off;
   const int64_t P = p.T * p.k;
   const bool lora = p.L > 0;
   const int BM = w.rows_per_item;   // rows of a work item
@@ -1859,10 +1863,10 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     const int64_t n4 = p.T * p.H / 4;
     const dim3 cg((unsigned)ceil_div(n4, 256));
     if (p.out_f32)
-      hipLaunchKernelGGL((combine_kernel<float, float>), cg, dim3(256), 0, stream, z,
+      hipLaunchKernelGGL((combine_kernel<kBf16, float>), cg, dim3(256), 0, stream, (const void*)z,
                          static_cast<float*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
     else
-      hipLaunchKernelGGL((combine_kernel<float, T>), cg, dim3(256), 0, stream, z,
+      hipLaunchKernelGGL((combine_kernel<kBf16, T>), cg, dim3(256), 0, stream, (const void*)z,
                          static_cast<T*>(p.y), p.T, (int)p.k, p.H, w.split_down_k, P * p.H);
   }
   mark(2 * kStageCombine + 1);
@@ -2022,11 +2026,11 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
   if (P > 0) {
     const int64_t n4 = P * N / 4;
     if (p.out_f32)
-      hipLaunchKernelGGL((combine_kernel<float, float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<float*>(p.y), P, 1, N, w.ksplit, P * N);
+      hipLaunchKernelGGL((combine_kernel<false, float>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, (const void*)z, static_cast<float*>(p.y), P, 1, N, w.ksplit, P * N);
     else
-      hipLaunchKernelGGL((combine_kernel<float, T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
-                         stream, z, static_cast<T*>(p.y), P, 1, N, w.ksplit, P * N);
+      hipLaunchKernelGGL((combine_kernel<false, T>), dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0,
+                         stream, (const void*)z, static_cast<T*>(p.y), P, 1, N, w.ksplit, P * N);
   }
   mark(2 * kDenseStageCombine + 1);
   return hipGetLastError();

@@ -43,16 +43,23 @@ constexpr int SPW = STAGE / 1024 / NW;      // DMA instructions per wave per sta
 constexpr int A_WAVES = BM * ROWB / 1024 / SPW;   // waves 0..3 load A rows, 4..7 weight rows
 constexpr int EXP_LD = 40;           // expand scratch: elements per column (32 ranks + pad)
 constexpr int EP_GU_LD = 40;         // gate_up epilogue staging: row stride in bf16
+#ifndef MOELORA_BIG_Z_ROWS
+#define MOELORA_BIG_Z_ROWS 32
+#endif
+constexpr int Z_ROWS = MOELORA_BIG_Z_ROWS;   // down epilogue staging: rows per pass and wave
+constexpr int EP_Z_LD = 68;          // and its row stride in fp32
 constexpr int LDS_BYTES = 2 * STAGE;
 static_assert(NW * 64 * EXP_LD * 2 <= STAGE, "expand scratch fits the second ring slot");
 static_assert(NW * WM * EP_GU_LD * 2 <= LDS_BYTES, "gate_up staging fits");
+constexpr int LDS_DOWN = NW * Z_ROWS * EP_Z_LD * 4 > LDS_BYTES ? NW * Z_ROWS * EP_Z_LD * 4 : LDS_BYTES;
+static_assert(LDS_DOWN + 4096 <= 160 * 1024 && WM % Z_ROWS == 0 && Z_ROWS % 16 == 0, "down staging fits");
 }  // namespace big
 
 template <bool GATE_UP>
 __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   using namespace big;
   typedef bf16_t T;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[GATE_UP ? LDS_BYTES : LDS_DOWN];
   __shared__ int ep_pid[BM];     // down epilogue: pair id of each tile row
   __shared__ float ep_w[BM];     // and its router weight
   __shared__ int claimed;
@@ -399,9 +406,9 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   next_desc = a.tile_tab[max(min(t_begin + __builtin_amdgcn_readfirstlane(claimed), t_end - 1), 0)];
   have_next = true;
 
-  // ---- epilogue: gate_up through this wave's LDS region so that every lane
-  // stores 16 contiguous bytes (a lane's accumulators hold one column of 4
-  // rows); the down GEMM's fp32 z rows are written from the accumulators
+  // ---- epilogue: through this wave's LDS region, so that every lane stores
+  // 16 contiguous bytes of act (gate_up) or 12 of z (down): a lane's
+  // accumulators hold one column of 4 rows
   if (GATE_UP) {
     T* ep = reinterpret_cast<T*>(lds) + wave * (WM * EP_GU_LD);
 #pragma unroll
@@ -430,22 +437,39 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
       ep_w[r] = a.topk_weights[min(pid, a.P - 1)];
     }
     __syncthreads();   // ep_pid / ep_w are written by other waves
-    // z rows straight from the accumulators, fp32: per (block, row) the wave's
-    // 16-lane groups each write one row's 16 columns (64 bytes), and the four
-    // column blocks of a row go out back to back (256 contiguous bytes)
+    // z rows in the 24-bit form (fp24_pack4), through this wave's LDS region
+    // in passes of Z_ROWS rows: the lanes stage their accumulators (a lane holds one
+    // column of 4 rows per block), then each takes 4 consecutive columns of
+    // one row, weights them and stores 12 bytes (16 lanes: one row's 64
+    // columns, 192 contiguous bytes)
+    char* zb = static_cast<char*>(a.z);
+    float* ep = reinterpret_cast<float*>(lds) + wave * (Z_ROWS * EP_Z_LD);
+    constexpr int BPP = Z_ROWS / 16;   // row blocks per pass
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int ps = 0; ps < MB / BPP; ++ps) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rloc = wm * WM + i * 16 + 4 * (lane >> 4) + v;
-        const int pid = ep_pid[rloc];
-        const float wgt = ep_w[rloc];
-        if (rloc >= nrows || pid >= a.P) continue;
-        float* zrow = a.z + ((int64_t)split * a.P + pid) * a.n_out + n0 + wn * WN + lrow;
+      for (int ii = 0; ii < BPP; ++ii)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          if (n0 + wn * WN + j * 16 + lrow < a.n_out) zrow[j * 16] = wgt * acc[i][j][v];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            ep[(ii * 16 + 4 * (lane >> 4) + v) * EP_Z_LD + j * 16 + lrow] = acc[BPP * ps + ii][j][v];
+      __builtin_amdgcn_wave_barrier();   // the wave's staging writes before its reads
+#pragma unroll
+      for (int c = lane; c < Z_ROWS * (WN / 4); c += 64) {
+        const int r = c / (WN / 4), cc = c % (WN / 4);
+        const int rloc = wm * WM + ps * Z_ROWS + r;
+        const int64_t col = n0 + wn * WN + cc * 4;
+        const int pid = ep_pid[rloc];
+        if (rloc >= nrows || pid >= a.P || col >= a.n_out) continue;
+        const float wgt = ep_w[rloc];
+        floatx4 vv = *reinterpret_cast<const floatx4*>(ep + r * EP_Z_LD + cc * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vv[q] = wgt * vv[q];
+        *reinterpret_cast<u32x3*>(zb + (((int64_t)split * a.P + pid) * a.n_out + col) * 3) = fp24_pack4(vv);
       }
+      __builtin_amdgcn_wave_barrier();   // and its reads before the next pass's writes
+    }
   }
   }();
   if (!published) {   // a skipped tile: publish here

@@ -33,7 +33,8 @@ struct GemmArgs {
   const T* b_pool1;           // [L, E, R, n_out] (up) or null
   // outputs
   T* act;                     // gate_up: [cap, n_out]
-  float* z;                   // down: [ksplit, P, n_out], one plane per K split (fp32)
+  void* z;                    // down: [ksplit, P, n_out] weighted rows, one plane per K split:
+                              // fp24 (fp24_pack4) for bf16 T, fp32 for fp32 T and dense mode
   const float* topk_weights;
   int64_t cap;                // rows of sorted_ids / act / h
   int32_t* tile_ctr;          // [8] per-XCD tile counters, zero at launch
