@@ -1409,11 +1409,15 @@ template <typename T> struct TileCfg;
 #ifndef MOELORA_BF16_BN
 #define MOELORA_BF16_BN 256
 #endif
+// 4 x 2 waves (32 rows x 128 columns each): a wave's rows span two 16-row
+// align blocks, so the LoRA expand makes at most two passes (one per slot)
+// instead of four; measured against 2 x 4 on decode and fine-grained batches:
+// GEMM stages 0.5-3% faster, from fewer expand passes
 #ifndef MOELORA_BF16_WM
-#define MOELORA_BF16_WM 2
+#define MOELORA_BF16_WM 4
 #endif
 #ifndef MOELORA_BF16_WN
-#define MOELORA_BF16_WN 4
+#define MOELORA_BF16_WN 2
 #endif
 #ifndef MOELORA_BF16_STAGES
 #define MOELORA_BF16_STAGES 3
