@@ -172,9 +172,22 @@ struct ShrinkArgs {
   const int32_t* num_rows_padded;
   const int32_t* lora_ranks;
   const float* scaling;
-  float* h;                   // [cap, npools * RP], fp32
+  float* h;                   // [cap, npools * RP]: fp32, or for bf16 T the final h split (store_h_split)
   int64_t cap;                // rows of h / act / sorted_ids
 };
+
+// The final h of a bf16 layer is stored split for the GEMM's expand, which
+// multiplies h = hi + lo on bf16 matrix cores: per row, each group of 8
+// consecutive columns takes the 32 bytes of 8 fp32 values as the 8 bf16 high
+// parts hi = bf16(v), then the 8 low parts lo = bf16(v - hi) (both round to
+// nearest even; v - hi is exact, so hi + lo keeps about 16 bits of v).
+// Partial sums of a K-split shrink stay fp32 until shrink_reduce adds them.
+__device__ inline void store_h_split(float* hrow, int c, float v) {
+  bf16_t* g = reinterpret_cast<bf16_t*>(hrow + (c & ~7));
+  const bf16_t hi = (bf16_t)v;
+  g[c & 7] = hi;
+  g[8 + (c & 7)] = (bf16_t)(v - (float)hi);
+}
 
 template <typename T, int NPOOL>
 __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
@@ -198,6 +211,8 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
   const float s = a.scaling[l];
   const int HS = NPOOL * a.RP;
   float* hrow_base = a.h + (int64_t)blockIdx.y * a.split_stride + row0 * HS;
+  // a bf16 layer without a K split writes its final h, split (else fp32 partials)
+  const bool split_h = sizeof(T) == 2 && gridDim.y == 1;
   if (r <= 0) {
     // rank-0 slots are folded into the no-LoRA bucket by align; keep h defined anyway
     for (int i = threadIdx.x; i < 16 * HS; i += 256) hrow_base[i] = 0.0f;
@@ -268,7 +283,10 @@ __global__ void __launch_bounds__(256) shrink_kernel(ShrinkArgs<T> a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = (lane >> 4) * 4 + i;
         float v = (qb < nqb && col < r) ? s * t[i] : 0.0f;
-        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
+        if (split_h)
+          store_h_split(hrow_base + (int64_t)rr * HS, pi * a.RP + col, v);
+        else
+          hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
       }
     }
 }
@@ -464,20 +482,42 @@ __global__ void __launch_bounds__(64 * NW) shrink4_kernel(ShrinkArgs<T> a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = (lane >> 4) * 4 + i;
         const float v = (qb < nqb && col < r) ? sc * t[i] : 0.0f;
-        hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
+        if (sizeof(T) == 2 && gridDim.y == 1)   // the final h of a bf16 layer: split (store_h_split)
+          store_h_split(hrow_base + (int64_t)rr * HS, pi * a.RP + col, v);
+        else
+          hrow_base[(int64_t)rr * HS + pi * a.RP + col] = v;
       }
     }
 }
 
-// h[0] += h[1] + ... + h[S-1] over the padded rows, in split order
+// h[0] += h[1] + ... + h[S-1] over the padded rows, in split order; with
+// split_h (a bf16 layer) the sum is stored split (store_h_split).  A thread
+// takes one group of 8 columns.
 __global__ void __launch_bounds__(256)
 shrink_reduce_kernel(float* __restrict__ h, int64_t split_stride, int splits,
-                     const int32_t* __restrict__ num_rows_padded, int HS) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+                     const int32_t* __restrict__ num_rows_padded, int HS, int split_h) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= (int64_t)num_rows_padded[0] * HS) return;
-  floatx4 v = *reinterpret_cast<const floatx4*>(h + i);
-  for (int sp = 1; sp < splits; ++sp) v += *reinterpret_cast<const floatx4*>(h + sp * split_stride + i);
-  *reinterpret_cast<floatx4*>(h + i) = v;
+  floatx4 v0 = *reinterpret_cast<const floatx4*>(h + i);
+  floatx4 v1 = *reinterpret_cast<const floatx4*>(h + i + 4);
+  for (int sp = 1; sp < splits; ++sp) {
+    v0 += *reinterpret_cast<const floatx4*>(h + sp * split_stride + i);
+    v1 += *reinterpret_cast<const floatx4*>(h + sp * split_stride + i + 4);
+  }
+  if (split_h) {
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = u < 4 ? v0[u] : v1[u - 4];
+      hi[u] = (bf16_t)v;
+      lo[u] = (bf16_t)(v - (float)hi[u]);
+    }
+    *reinterpret_cast<bf16x8*>(h + i) = hi;
+    *reinterpret_cast<bf16x8*>(h + i + 4) = lo;
+  } else {
+    *reinterpret_cast<floatx4*>(h + i) = v0;
+    *reinterpret_cast<floatx4*>(h + i + 4) = v1;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -1068,15 +1108,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
             const bool mine = lg[i][lrow / 16] == l;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
+              // h arrives split (store_h_split): the 32 bytes of this lane's 8
+              // ranks are their 8 bf16 high parts, then the 8 low parts; rows
+              // of another slot contribute zero
               const floatx8 hv = second_of(j) ? hu[i] : hg[i];
-              // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
-              frag hi, lo;
-#pragma unroll
-              for (int v = 0; v < 8; ++v) {
-                const float x = mine ? hv[v] : 0.0f;
-                hi[v] = (bf16_t)x;
-                lo[v] = (bf16_t)(x - (float)hi[v]);
-              }
+              const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+              const floatx4 h0 = {hv[0], hv[1], hv[2], hv[3]}, h1 = {hv[4], hv[5], hv[6], hv[7]};
+              const frag hi = __builtin_bit_cast(frag, mine ? h0 : z4);
+              const frag lo = __builtin_bit_cast(frag, mine ? h1 : z4);
               acc[i][j] = B_::mma(hi, bfr[j], acc[i][j]);
               acc[i][j] = B_::mma(lo, bfr[j], acc[i][j]);
             }
@@ -1143,19 +1182,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) gemm_kernel(GemmArgs<T
       for (int j = 0; j < NB; ++j) {
         const bool up = GATE_UP ? j >= NB / 2 : dense_second(j);
         const floatx8& hv = up ? hu : hg;
-        if constexpr (sizeof(T) == 2) {
-          // h = hi + lo with both halves exact in bf16: the expand keeps ~16 bits of h
-          frag hi, lo;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            hi[v] = (bf16_t)hv[v];
-            lo[v] = (bf16_t)(hv[v] - (float)hi[v]);
-          }
-          acc[i][j] = B_::mma(hi, bfv[j], acc[i][j]);
-          acc[i][j] = B_::mma(lo, bfv[j], acc[i][j]);
-        } else {
-          acc[i][j] = B_::mma(hv, bfv[j], acc[i][j]);
-        }
+        acc[i][j] = B_::mma(hv, bfv[j], acc[i][j]);   // fp32 layers: h in fp32
       }
     };
     // one pass: rank steps from ks0 on (ks0 = 1: step 0 already done)
@@ -1738,9 +1765,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.split_stride = w.cap * 2 * w.RP;
     launch_shrink<T, 2>(s, groups, w.split_gu, w.shrink4, stream);
     if (w.split_gu > 1)
-      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * 2 * w.RP / 4, 256)),
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * 2 * w.RP / 8, 256)),
                          dim3(256), 0, stream, hgu, (int64_t)s.split_stride, w.split_gu,
-                         p.num_rows_padded, (int)(2 * w.RP));
+                         p.num_rows_padded, (int)(2 * w.RP), kBf16 ? 1 : 0);
   }
   mark(2 * kStageShrinkX + 1);
 
@@ -1818,9 +1845,9 @@ static hipError_t run_forward(const ForwardProblem& p, void* workspace, hipStrea
     s.split_stride = w.cap * w.RP;
     launch_shrink<T, 1>(s, groups, w.split_d, w.shrink4, stream);
     if (w.split_d > 1)
-      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.RP / 4, 256)),
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.RP / 8, 256)),
                          dim3(256), 0, stream, hd, (int64_t)s.split_stride, w.split_d,
-                         p.num_rows_padded, (int)w.RP);
+                         p.num_rows_padded, (int)w.RP, kBf16 ? 1 : 0);
   }
   mark(2 * kStageShrinkA + 1);
   // down
@@ -1977,9 +2004,9 @@ static hipError_t run_dense(const DenseProblem& p, void* workspace, hipStream_t 
     else
       launch_shrink<T, 1>(s, groups, w.split, false, stream);
     if (w.split > 1)
-      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.npool * w.RP / 4, 256)),
+      hipLaunchKernelGGL(shrink_reduce_kernel, dim3((unsigned)ceil_div(w.cap * w.npool * w.RP / 8, 256)),
                          dim3(256), 0, stream, h, (int64_t)s.split_stride, w.split,
-                         p.num_rows_padded, (int)(w.npool * w.RP));
+                         p.num_rows_padded, (int)(w.npool * w.RP), std::is_same<T, bf16_t>::value ? 1 : 0);
   }
   mark(2 * kDenseStageShrink + 1);
 

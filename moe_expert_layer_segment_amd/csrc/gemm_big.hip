@@ -222,7 +222,8 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
   // 16-byte load per lane and chunk, turns them into MFMA fragments through a
   // wave-private scratch in the second ring slot (filled by DMA only after
   // the barrier below), and multiplies the rows of each block holding the
-  // slot: h = hi + lo, both exact in bf16 (about 16 bits of h survive).
+  // slot: h = hi + lo, both bf16, stored split by the shrink (about 16 bits
+  // of h survive).
   // Rank rows >= r and columns >= n_out are zero, never read.
   if (lora_here) {
     T* bt = reinterpret_cast<T*>(lds + STAGE) + wave * (64 * EXP_LD);
@@ -304,13 +305,11 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmArgs<bf16_t> a) {
             if (slot_of(i) != l) return;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-              const floatx8 hv = (GATE_UP && j >= NB / 2) ? hu[ii] : hg[ii];
-              bf16x8 hi, lo;
-#pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                hi[u] = (T)hv[u];
-                lo[u] = (T)(hv[u] - (float)hi[u]);
-              }
+              // h arrives split: the 32 bytes of the lane's 8 ranks hold their
+              // 8 bf16 high parts, then the 8 low parts
+              const int4v* hw = reinterpret_cast<const int4v*>((GATE_UP && j >= NB / 2) ? &hu[ii] : &hg[ii]);
+              const bf16x8 hi = __builtin_bit_cast(bf16x8, hw[0]);
+              const bf16x8 lo = __builtin_bit_cast(bf16x8, hw[1]);
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bfr[j], acc[i][j], 0, 0, 0);
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bfr[j], acc[i][j], 0, 0, 0);
             }

@@ -27,7 +27,7 @@ struct GemmArgs {
   const int32_t* expert_tile_offsets;   // [E+1], in align blocks of BM_tile rows
   int BM_tile;
   const int32_t* lora_ranks;
-  const float* h;             // [cap, HS], fp32 (scaled shrink result)
+  const float* h;             // [cap, HS] scaled shrink result: fp32 (fp32 T) or split bf16 halves (store_h_split)
   int HS, RP, R, L, E;
   const T* b_pool0;           // [L, E, R, n_out] (gate or down)
   const T* b_pool1;           // [L, E, R, n_out] (up) or null
