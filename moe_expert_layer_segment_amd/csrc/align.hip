@@ -35,7 +35,8 @@ int align_waves_for_keys(int64_t K) {
 
 // 64-pair steps per wave: as many as keep the chunk count near 16, so a
 // small batch spreads over several workgroups instead of walking its pairs
-// step by step in one (the scan's cost grows with chunks x keys)
+// step by step in one (the scan's cost grows with chunks x keys: targets of
+// 32, 64 and 128 chunks measured align on c2 at 42, 58 and 91 us against 38)
 int align_steps(int64_t P, int64_t K) {
   const int64_t per_step = (int64_t)align_waves_for_keys(K) * 64;
   return (int)std::min<int64_t>(kAlignSteps, std::max<int64_t>(1, ceil_div(P, per_step * 16)));
@@ -171,68 +172,60 @@ align_scan_kernel(int nchunks, int K, int E, int L, int BM, int32_t* __restrict_
   __shared__ int lds_waves[kScanThreads / 64 + 1];
   const int kpt = (K + kScanThreads - 1) / kScanThreads;
   const int k0 = min(K, (int)threadIdx.x * kpt), k1 = min(K, k0 + kpt);
-  // A thread's keys k0..k1-1 are scanned over the chunks in place.  Loads and
-  // stores of one array keep their program order, so a key-by-key loop waits
-  // for memory once per key; when the thread's block of counts is small
-  // (decode-sized batches) it is read into registers first, all at once.
-  constexpr int KB = 8, CB = 8;
-  const bool small = kpt <= KB && nchunks <= CB;   // uniform
-  int v[KB][CB], tot[KB];
+  // A thread's keys k0..k1-1 are scanned over the chunks in place (each
+  // chunk's count becomes the key's count in the chunks before it), KB keys
+  // and CB chunks at a time: the block's loads all go out before the first
+  // use, one memory round trip per block (a key-by-key, chunk-by-chunk loop
+  // waits for each load: its next load cannot pass the store before it).
+  // The key's first row is added by the scatter, not here.
+  constexpr int KB = 4, CB = 8;
+  int tot[KB] = {0, 0, 0, 0};   // the totals of the first KB keys (all of them when kpt <= KB)
   int mine = 0;
-  if (small) {
+  for (int kb = k0; kb < k1; kb += KB) {
+    int run[KB];
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
+    for (int kk = 0; kk < KB; ++kk) run[kk] = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += CB) {
+      int v[KB][CB];
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-        v[kk][c] = (k0 + kk < k1 && c < nchunks) ? ws_cnt[(int64_t)c * K + k0 + kk] : 0;
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          v[kk][c] = (kb + kk < k1 && c0 + c < nchunks) ? ws_cnt[(int64_t)(c0 + c) * K + kb + kk] : 0;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          const int x = v[kk][c];
+          v[kk][c] = run[kk];
+          run[kk] += x;
+        }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          if (kb + kk < k1 && c0 + c < nchunks) ws_cnt[(int64_t)(c0 + c) * K + kb + kk] = v[kk][c];
+    }
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-      int run = 0;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int x = v[kk][c];
-        v[kk][c] = run;
-        run += x;
-      }
-      tot[kk] = run;
-      if (k0 + kk < k1) mine += (int)round_up(run, BM);
-    }
-  } else {
-    for (int key = k0; key < k1; ++key) {
-      int run = 0;
-      for (int c = 0; c < nchunks; ++c) {
-        int64_t idx = (int64_t)c * K + key;
-        int x = ws_cnt[idx];
-        ws_cnt[idx] = run;
-        run += x;
-      }
-      ws_btotal[key] = run;
-      mine += (int)round_up(run, BM);
+      if (kb + kk >= k1) continue;
+      ws_btotal[kb + kk] = run[kk];
+      mine += (int)round_up(run[kk], BM);
+      if (kb == k0) tot[kk] = run[kk];
     }
   }
   int total = 0;
   int start = block_exclusive_scan(mine, lds_waves, &total);
-  if (small) {
+  // the first KB keys' totals are in registers, further ones (kpt > KB) are read back
+  auto place = [&](int key, int key_total) {
+    ws_bstart[key] = start;
+    if (key % (L + 1) == 0) expert_tile_offsets[key / (L + 1)] = start / BM;   // the expert's first key
+    start += (int)round_up(key_total, BM);
+  };
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int key = k0 + kk;
-      if (key >= k1) continue;
-      ws_btotal[key] = tot[kk];
-      ws_bstart[key] = start;
-      if (key % (L + 1) == 0) expert_tile_offsets[key / (L + 1)] = start / BM;   // the expert's first key
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-        if (c < nchunks) ws_cnt[(int64_t)c * K + key] = v[kk][c] + start;
-      start += (int)round_up(tot[kk], BM);
-    }
-  } else {
-    for (int key = k0; key < k1; ++key) {
-      ws_bstart[key] = start;
-      if (key % (L + 1) == 0) expert_tile_offsets[key / (L + 1)] = start / BM;   // the expert's first key
-      for (int c = 0; c < nchunks; ++c) ws_cnt[(int64_t)c * K + key] += start;
-      start += (int)round_up(ws_btotal[key], BM);
-    }
-  }
+  for (int kk = 0; kk < KB; ++kk)
+    if (k0 + kk < k1) place(k0 + kk, tot[kk]);
+  for (int key = k0 + KB; key < k1; ++key) place(key, ws_btotal[key]);
   if (threadIdx.x == 0) {
     ws_bstart[K] = total;
     num_rows_padded[0] = total;
@@ -251,7 +244,8 @@ align_scatter_kernel(int P, int k, int E, int L, int K, int BM, int64_t cap, int
   if (i < P) {
     int key = pair_key((int)i, k, E, L, topk_ids, mapping, enabled);
     if (key >= 0) {
-      int64_t pos = (int64_t)ws_off[(i / chunk_pairs) * K + key] + ws_rank[i];
+      // the key's first row + the key's pairs in earlier chunks + the rank in this chunk
+      int64_t pos = (int64_t)ws_bstart[key] + ws_off[(i / chunk_pairs) * K + key] + ws_rank[i];
       if (pos >= 0 && pos < cap) sorted_ids[pos] = (int32_t)i;
     }
   }
