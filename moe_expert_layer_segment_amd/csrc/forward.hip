@@ -6,14 +6,17 @@
 //   plan     -- one workgroup turns expert_tile_offsets into GEMM work items
 //               (row ranges of one expert, at most kBM rows each).
 //   shrink_x -- per 16-row group with an adapter: h_gu = s * [x A_g^T | x A_u^T]
-//               (rank columns beyond the slot rank are zero).
+//               (rank columns beyond the slot rank are zero; a bf16 layer stores h
+//               as its bf16 high and low halves, store_h_split).
 //   gate_up  -- grouped MFMA GEMM over the work items: x rows gathered by pair id
 //               times W_gate / W_up rows; LoRA expand h_g B_g, h_u B_u added to the
 //               accumulators of each 16-row group; SiLU(gate) * up epilogue -> act.
 //   shrink_a -- h_d = s * act A_d^T per 16-row group.
 //   down     -- grouped MFMA GEMM act * W_down^T + h_d B_d, times the router weight,
-//               written to z in pair order (fp32).
-//   combine  -- y[t] = sum_j z[t*k + j] for j = 0..k-1 in order (fp32), cast to dtype.
+//               written to z in pair order (fp32 layers: fp32; bf16 layers: the
+//               top 24 bits of the fp32 value, fp24_pack4).
+//   combine  -- y[t] = sum_j z[t*k + j] for j = 0..k-1 in order, summed in fp32,
+//               cast to the output dtype.
 #include <hip/hip_ext.h>
 
 #include <mutex>
